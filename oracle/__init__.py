@@ -1,0 +1,179 @@
+"""CPU oracle of the R-KV eviction step — TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The HIP library never uses it.
+
+``rkv_oracle.cpp`` is plain single-threaded C++ in double precision, built
+with g++ into ``librkv_oracle.so`` next to this file; this module is only its
+ctypes marshalling. Every function is pinned by the ``-m "not gpu"`` tests
+(hand-derived closed forms, textbook special cases, invariants, brute force).
+Parity unpinned by the pages themselves: the exact combination formula and
+the exact protection rule, which the R-KV page does not print; the oracle
+follows the readings stated in its source.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rkv_oracle.cpp")
+_HDR = os.path.join(_HERE, "rkv_oracle.h")
+_LIB_PATH = os.path.join(_HERE, "librkv_oracle.so")
+
+ORC_BF16 = 0
+ORC_F32 = 1
+
+
+def build(force: bool = False) -> str:
+    """Compiles the oracle with g++ -O2 (no fast-math, no OpenMP, no SIMD intrinsics)."""
+    newest = max(os.path.getmtime(_SRC), os.path.getmtime(_HDR))
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < newest:
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", _SRC, "-o", tmp])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _SliceParams(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("obs_window", ctypes.c_int32), ("budget", ctypes.c_int32), ("beta", ctypes.c_int32),
+                ("lam", ctypes.c_double), ("tau", ctypes.c_double), ("amb_eps", ctypes.c_double)]
+
+
+class _SliceOut(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("importance", "rowmean", "counts", "rbar", "R", "Z", "ambiguous", "keep")]
+
+
+class _StepParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("num_layers", "batch", "num_kv_heads", "group", "head_dim", "capacity", "budget", "buffer",
+                 "obs_window", "beta")] + [("lam", ctypes.c_double), ("tau", ctypes.c_double)]
+
+
+_lib = None
+
+
+def load_library(path: str):
+    """Loads an oracle shared library built from rkv_oracle.cpp and declares its C signatures."""
+    L = ctypes.CDLL(path)
+    L.orc_slice.restype = ctypes.c_int32
+    L.orc_slice.argtypes = [ctypes.POINTER(_SliceParams), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                            ctypes.POINTER(_SliceOut)]
+    L.orc_evict_step.restype = ctypes.c_int32
+    L.orc_evict_step.argtypes = [ctypes.POINTER(_StepParams), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.orc_gather_rows.restype = None
+    L.orc_gather_rows.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_void_p]
+    return L
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        _lib = load_library(_LIB_PATH)
+    return _lib
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return ORC_BF16
+    if a.dtype == np.float32:
+        return ORC_F32
+    raise TypeError(f"oracle inputs are bf16 bits (uint16) or float32, got {a.dtype}")
+
+
+@dataclass
+class SliceResult:
+    kept: int
+    keep: np.ndarray  # positions within the slice, ascending
+    importance: Optional[np.ndarray] = None
+    rowmean: Optional[np.ndarray] = None
+    counts: Optional[np.ndarray] = None
+    rbar: Optional[np.ndarray] = None
+    R: Optional[np.ndarray] = None
+    Z: Optional[np.ndarray] = None
+    ambiguous: Optional[np.ndarray] = None
+
+
+def slice_eval(keys: np.ndarray, queries: np.ndarray, budget: int, obs_window: int = 8, beta: int = 2,
+               lam: float = 0.1, tau: float = 0.5, amb_eps: float = 0.0) -> SliceResult:
+    """Scores and selects one slice.
+
+    keys: [N, D]; queries: [G, alpha, D] (or [G*alpha, D]); both bf16 bits
+    (uint16) or float32. Scores are returned only when N > budget.
+    """
+    keys = np.ascontiguousarray(keys)
+    queries = np.ascontiguousarray(queries)
+    code = _dtype_code(keys)
+    assert _dtype_code(queries) == code
+    N, D = keys.shape
+    G = queries.size // (obs_window * D)
+    assert G * obs_window * D == queries.size
+    p = _SliceParams(N, D, G, obs_window, budget, beta, lam, tau, amb_eps)
+    nk = min(N, budget)
+    keep = np.zeros(max(nk, 1), dtype=np.int32)
+    res = SliceResult(kept=0, keep=keep)
+    out = _SliceOut()
+    out.keep = keep.ctypes.data
+    if N > budget:
+        res.importance = np.zeros(N)
+        res.rowmean = np.zeros(N)
+        res.counts = np.zeros(N, dtype=np.int32)
+        res.rbar = np.zeros(N)
+        res.R = np.zeros(N)
+        res.Z = np.zeros(N)
+        res.ambiguous = np.zeros(N, dtype=np.int32)
+        for name in ("importance", "rowmean", "counts", "rbar", "R", "Z", "ambiguous"):
+            setattr(out, name, getattr(res, name).ctypes.data)
+    kept = lib().orc_slice(ctypes.byref(p), code, keys.ctypes.data, queries.ctypes.data, ctypes.byref(out))
+    if kept < 0:
+        raise ValueError("oracle rejected the slice parameters")
+    res.kept = kept
+    res.keep = keep[:kept].copy()
+    return res
+
+
+def evict_step(K: np.ndarray, V: np.ndarray, Q: np.ndarray, seq_start: np.ndarray, n_slots: int, budget: int,
+               buffer: int = 128, obs_window: int = 8, beta: int = 2, lam: float = 0.1, tau: float = 0.5):
+    """One eviction step in place on host arrays K, V: [L][b][H][C][D].
+
+    Returns (evicted: bool, n_slots_after, keep [L][b][H][B] source slots or -1).
+    seq_start is updated in place.
+    """
+    assert K.shape == V.shape and K.dtype == V.dtype
+    assert K.flags["C_CONTIGUOUS"] and V.flags["C_CONTIGUOUS"] and seq_start.dtype == np.int32
+    Q = np.ascontiguousarray(Q)
+    code = _dtype_code(K)
+    L_, Bt, H, C, D = K.shape
+    G = Q.shape[2] // H
+    p = _StepParams(L_, Bt, H, G, D, C, budget, buffer, obs_window, beta, lam, tau)
+    kptrs = (ctypes.c_void_p * L_)(*[K[l].ctypes.data for l in range(L_)])
+    vptrs = (ctypes.c_void_p * L_)(*[V[l].ctypes.data for l in range(L_)])
+    ns = ctypes.c_int32(n_slots)
+    keep = np.full((L_, Bt, H, budget), -1, dtype=np.int32)
+    rc = lib().orc_evict_step(ctypes.byref(p), code, ctypes.cast(kptrs, ctypes.c_void_p),
+                              ctypes.cast(vptrs, ctypes.c_void_p), Q.ctypes.data, seq_start.ctypes.data,
+                              ctypes.addressof(ns), keep.ctypes.data)
+    if rc < 0:
+        raise ValueError("oracle rejected the step parameters")
+    return rc == 1, ns.value, keep
+
+
+def gather_rows(src: np.ndarray, keep: np.ndarray) -> np.ndarray:
+    """dst[j] = src[keep[j]] for keep[j] >= 0; dst rows with keep[j] < 0 are zero."""
+    src = np.ascontiguousarray(src)
+    keep = np.ascontiguousarray(keep, dtype=np.int32)
+    dst = np.zeros((keep.shape[0],) + src.shape[1:], dtype=src.dtype)
+    row_bytes = src.strides[0]
+    lib().orc_gather_rows(src.ctypes.data, keep.ctypes.data, keep.shape[0], row_bytes, dst.ctypes.data)
+    return dst

@@ -1,0 +1,93 @@
+/*
+ * CPU oracle of the R-KV decode-time eviction step — TEST INFRASTRUCTURE.
+ *
+ * Plain, slow, single-threaded C++ in double precision. Only the tests, the
+ * smoke check and the benchmark's CPU-baseline leg use it; the HIP library
+ * never links, loads or calls it, and it shares no code with that library.
+ *
+ * Sources (the R-KV pages):
+ *   [RKV] R-KV notes page, yoonschallenge.tistory.com/1236 (NeurIPS 2025
+ *         poster): opening notes, summary table, Q&A part 2 ("why did time
+ *         drop less than expected"), cause 3 (per-128-token compression work).
+ * Where the pages are silent (the combination formula, the protection rule,
+ * tie order, padding) the readings below are stated at the point of use.
+ *
+ * Parity pins: every function is pinned by the CPU tests against hand-derived
+ * closed forms, textbook special cases, invariants and brute force.
+ */
+#ifndef RKV_ORACLE_H
+#define RKV_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORC_BF16 0
+#define ORC_F32 1
+
+/* One slice = one (layer, sequence, KV head). */
+typedef struct {
+  int32_t n;          /* valid tokens N of the slice                       */
+  int32_t head_dim;   /* D                                                 */
+  int32_t group;      /* G query heads per KV head                         */
+  int32_t obs_window; /* alpha, observation tokens kept unconditionally    */
+  int32_t budget;     /* B, kept tokens after eviction (window included)   */
+  int32_t beta;       /* protection count                                  */
+  double lambda;      /* weight of importance in Z = lambda*I - (1-lambda)*R */
+  double tau;         /* similarity threshold: "similar" means S_ij > tau  */
+  double amb_eps;     /* |S_ij - tau| <= amb_eps flags row min(i,j) as ambiguous */
+} orc_slice_params;
+
+/* Outputs of orc_slice; every pointer is nullable, arrays have N entries
+ * except keep (min(N, B) entries). */
+typedef struct {
+  double* importance; /* I_j for every valid j                              */
+  double* rowmean;    /* (1/(N-1)) * sum_{j != i} S_ij                      */
+  int32_t* counts;    /* c_i = #{ j > i : S_ij > tau }                      */
+  double* rbar;       /* 0 if c_i < beta, else rowmean_i                    */
+  double* R;          /* softmax of rbar over the candidates, 0 elsewhere   */
+  double* Z;          /* lambda*I - (1-lambda)*R over candidates, 0 elsewhere */
+  int32_t* ambiguous; /* 1 where a pair (i, j>i) sits within amb_eps of tau  */
+  int32_t* keep;      /* kept positions (0-based within the slice), ascending */
+} orc_slice_out;
+
+/*
+ * Scores and selects one slice. keys: N rows of D values; queries: G*alpha
+ * rows of D values (query head g, observation token t at row g*alpha + t;
+ * token t sits at position N - alpha + t). dtype ORC_BF16 (uint16 bits) or
+ * ORC_F32. When N <= B every token is kept and no score is computed.
+ * Returns the number of kept positions, or -1 on invalid parameters.
+ */
+int32_t orc_slice(const orc_slice_params* p, int32_t dtype, const void* keys, const void* queries,
+                  orc_slice_out* out);
+
+/* Whole-step parameters, mirroring the HIP library's parameter block. */
+typedef struct {
+  int32_t num_layers, batch, num_kv_heads, group, head_dim;
+  int32_t capacity; /* slots per [sequence][head] row block */
+  int32_t budget, buffer, obs_window, beta;
+  double lambda, tau;
+} orc_step_params;
+
+/*
+ * One eviction step over a batch of per-layer caches in host memory.
+ * k_layers[l], v_layers[l]: [batch][kv_head][capacity][D] (dtype as above);
+ * queries: [layer][batch][kv_head*G][alpha][D]; seq_start[b]: first valid slot
+ * of sequence b (in/out); *n_slots: slot count of every sequence (in/out).
+ * Below the trigger (*n_slots < budget + buffer) nothing changes and 0 is
+ * returned. Otherwise each slice keeps min(N_b, B) tokens, written in their
+ * original order to slots [B - kept, B); keep_out (nullable,
+ * [layer][batch][kv_head][B]) receives source slots, -1 for padding.
+ * Returns 1 when an eviction happened, -1 on invalid parameters.
+ */
+int32_t orc_evict_step(const orc_step_params* p, int32_t dtype, void* const* k_layers, void* const* v_layers,
+                       const void* queries, int32_t* seq_start, int32_t* n_slots, int32_t* keep_out);
+
+/* dst row j <- src row keep[j] for keep[j] >= 0 (out of place). */
+void orc_gather_rows(const void* src, const int32_t* keep, int32_t n_keep, int32_t row_bytes, void* dst);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

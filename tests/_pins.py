@@ -1,0 +1,320 @@
+"""Pins of the CPU oracle: checks against what the R-KV pages and mathematics fix.
+
+Each check raises AssertionError on a mismatch. They run against whatever
+library ``oracle.lib()`` returns, so the mutant tests can point them at a copy
+of the oracle with a planted mistake and require that some check fails.
+
+Kinds of pin (none of them re-types the oracle's own loops):
+  * hand-derived cases with exact closed forms (tests/golden/hand_cases.json);
+  * textbook special cases computed with library routines (torch float64
+    softmax / mean / amax / topk; scipy softmax);
+  * closed-form identities (row-mean identity through the sum of unit keys);
+  * invariants (budget, window, ordering, exact duplicates, orthogonal keys,
+    bitwise scale invariance, probability sums);
+  * brute force over all k-subsets on tiny inputs.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_cases.json")
+
+
+def _ev(expr: str) -> float:
+    """Evaluates a closed-form string of the golden file (fractions, e, exp)."""
+    if all(ch in "0123456789/-" for ch in expr):
+        return float(Fraction(expr))
+    return float(eval(expr, {"__builtins__": {}}, {"e": math.e, "exp": math.exp}))
+
+
+def _close(a, b, tol=1e-12, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}\n got {a}\n exp {b}"
+
+
+def golden_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+def _pad(arr, d):
+    arr = np.asarray(arr, dtype=np.float32)
+    out = np.zeros(arr.shape[:-1] + (d,), dtype=np.float32)
+    out[..., : arr.shape[-1]] = arr
+    return out
+
+
+def check_hand_case(case, pad_to: int = 0):
+    keys = np.asarray(case["keys"], dtype=np.float32)
+    q = np.asarray(case["queries"], dtype=np.float32)
+    if pad_to:
+        # zero padding keeps every dot product and cosine; the attention
+        # scale changes, so only zero-query cases are padded
+        assert not np.any(q)
+        keys, q = _pad(keys, pad_to), _pad(q, pad_to)
+    r = oracle.slice_eval(keys, q, budget=case["budget"], obs_window=case["obs_window"], beta=case["beta"],
+                          lam=case["lambda"], tau=case["tau"])
+    name = case["name"]
+    assert list(r.keep) == case["keep"], f"{name}: keep {list(r.keep)} != {case['keep']}"
+    n_c = keys.shape[0] - case["obs_window"]
+    if "counts" in case:
+        assert list(r.counts) == case["counts"], f"{name}: counts {list(r.counts)} != {case['counts']}"
+    if "rowmean" in case:
+        _close(r.rowmean, [_ev(x) for x in case["rowmean"]], what=f"{name} rowmean")
+    if "rbar" in case:
+        _close(r.rbar, [_ev(x) for x in case["rbar"]], what=f"{name} rbar")
+    if "importance" in case:
+        exp_i = [_ev(x) for x in case["importance"]]
+        _close(r.importance[: len(exp_i)], exp_i, what=f"{name} importance")
+    if "R_candidates" in case:
+        exp_r = [_ev(x) for x in case["R_candidates"]]
+        _close(r.R[:n_c], exp_r, what=f"{name} R")
+        exp_z = [case["lambda"] * r.importance[i] - (1 - case["lambda"]) * exp_r[i] for i in range(n_c)]
+        _close(r.Z[:n_c], exp_z, what=f"{name} Z")
+
+
+def check_hand_cases():
+    for case in golden_cases():
+        check_hand_case(case)
+        if not np.any(np.asarray(case["queries"])):
+            check_hand_case(case, pad_to=128)
+
+
+def _rand_slice(seed, n, d, g, alpha, dtype="bf16", scale=1.0):
+    rng = np.random.default_rng(seed)
+    k = (rng.standard_normal((n, d)) * scale).astype(np.float32)
+    q = rng.standard_normal((g, alpha, d)).astype(np.float32)
+    if dtype == "bf16":
+        return synth.bf16_bits(k), synth.bf16_bits(q)
+    return k, q
+
+
+def check_lambda1_textbook():
+    """lambda = 1: Z = I, so the kept candidates are the top-k of the GQA-max of
+    the mean causal attention, built here from torch float64 primitives."""
+    import torch
+
+    for seed, (n, d, g, alpha, budget) in enumerate([(40, 16, 3, 4, 24), (70, 32, 5, 8, 40), (33, 8, 1, 1, 20)]):
+        k_bits, q_bits = _rand_slice(100 + seed, n, d, g, alpha)
+        r = oracle.slice_eval(k_bits, q_bits, budget=budget, obs_window=alpha, lam=1.0)
+        K = torch.from_numpy(synth.to_float(k_bits, "bf16"))
+        Qm = torch.from_numpy(synth.to_float(q_bits, "bf16"))  # [g, alpha, d]
+        logits = torch.einsum("gtd,jd->gtj", Qm, K) / math.sqrt(d)
+        pos = torch.arange(n - alpha, n).view(1, alpha, 1)
+        mask = torch.arange(n).view(1, 1, n) > pos
+        attn = torch.softmax(logits.masked_fill(mask, float("-inf")), dim=-1)
+        imp = attn.mean(dim=1).amax(dim=0)
+        _close(r.importance, imp.numpy(), tol=1e-12, what=f"lambda1 importance seed {seed}")
+        cand = imp[: n - alpha]
+        top = torch.topk(cand, budget - alpha).indices.tolist()
+        exp_keep = sorted(top + list(range(n - alpha, n)))
+        assert list(r.keep) == exp_keep, f"lambda1 keep seed {seed}"
+
+
+def check_single_query_softmax():
+    """G = 1, alpha = 1: importance is one textbook softmax row (scipy)."""
+    from scipy.special import softmax
+
+    k_bits, q_bits = _rand_slice(7, 50, 64, 1, 1, dtype="f32")
+    r = oracle.slice_eval(k_bits, q_bits, budget=30, obs_window=1)
+    logits = (k_bits.astype(np.float64) @ q_bits.reshape(-1).astype(np.float64)) / 8.0
+    _close(r.importance, softmax(logits), tol=1e-12, what="single-query softmax")
+
+
+def check_probability_sums():
+    """Attention rows sum to 1, so with G = 1 the importance sums to 1; the
+    redundancy softmax sums to 1 over the candidates."""
+    k_bits, q_bits = _rand_slice(11, 90, 32, 1, 6)
+    r = oracle.slice_eval(k_bits, q_bits, budget=50, obs_window=6)
+    assert abs(r.importance.sum() - 1.0) < 1e-12, r.importance.sum()
+    assert abs(r.R[:84].sum() - 1.0) < 1e-12
+    assert np.all(r.R[84:] == 0.0)
+
+
+def check_rowmean_identity():
+    """sum_{j != i} S_ij = khat_i . (sum_j khat_j) - khat_i . khat_i."""
+    for seed in range(3):
+        k_bits, q_bits = _rand_slice(20 + seed, 64, 16, 2, 4)
+        r = oracle.slice_eval(k_bits, q_bits, budget=40, obs_window=4)
+        K = synth.to_float(k_bits, "bf16")
+        Kh = K / np.linalg.norm(K, axis=1, keepdims=True)
+        s = Kh.sum(axis=0)
+        ident = (Kh @ s - np.einsum("id,id->i", Kh, Kh)) / (K.shape[0] - 1)
+        _close(r.rowmean, ident, tol=1e-12, what="row-mean identity")
+
+
+def _basis_keys(n, d, rng, scales=True):
+    assert n <= d
+    perm = rng.permutation(d)[:n]
+    k = np.zeros((n, d), dtype=np.float32)
+    for i, c in enumerate(perm):
+        k[i, c] = (rng.uniform(0.5, 4.0) if scales else 1.0) * rng.choice([-1.0, 1.0])
+    return k
+
+
+def check_exact_duplicates():
+    """A cluster of m identical keys among mutually orthogonal keys: S = 1
+    inside the cluster, 0 elsewhere; exactly the min(m, beta) newest members
+    are protected; an unprotected member has redundancy (m-1)/(N-1)."""
+    rng = np.random.default_rng(5)
+    for m, beta in [(2, 2), (3, 2), (5, 2), (4, 1), (4, 3)]:
+        n, d, alpha = 40, 64, 4
+        k = _basis_keys(n, d, rng)
+        members = sorted(rng.choice(n - alpha, size=m, replace=False).tolist())
+        proto = np.zeros(d, dtype=np.float32)
+        used = set(np.nonzero(k)[1].tolist())
+        free = [c for c in range(d) if c not in used]
+        proto[free[0]] = 1.0
+        proto[free[1]] = -2.0
+        for i in members:
+            k[i] = proto * rng.choice([0.5, 1.0, 2.0])  # positive rescale: identical direction
+        q = rng.standard_normal((1, alpha, d)).astype(np.float32)
+        r = oracle.slice_eval(k, q, budget=20, obs_window=alpha, beta=beta)
+        for rank, i in enumerate(members):
+            newer = m - 1 - rank
+            assert r.counts[i] == newer, (m, beta, i, r.counts[i], newer)
+            if newer < beta:
+                assert r.rbar[i] == 0.0
+            else:
+                assert abs(r.rbar[i] - (m - 1) / (n - 1)) < 1e-12
+        others = [i for i in range(n) if i not in members]
+        assert np.all(r.counts[others] == 0) and np.all(r.rbar[others] == 0.0)
+
+
+def check_orthogonal_keys():
+    """Orthogonal keys: no similar pair, all protected, R = 1/|C| exactly,
+    selection is the top-k of importance."""
+    rng = np.random.default_rng(9)
+    n, d, alpha, budget = 48, 64, 8, 24
+    k = _basis_keys(n, d, rng)
+    q = rng.standard_normal((2, alpha, d)).astype(np.float32)
+    r = oracle.slice_eval(k, q, budget=budget, obs_window=alpha)
+    nc = n - alpha
+    assert np.all(r.counts == 0) and np.all(r.rbar == 0.0)
+    _close(r.R[:nc], np.full(nc, 1.0 / nc), tol=1e-15, what="orthogonal R")
+    top = np.argsort(-r.importance[:nc], kind="stable")[: budget - alpha]
+    assert list(r.keep) == sorted(top.tolist() + list(range(nc, n)))
+
+
+def check_scale_invariance():
+    """Keys times 2 and queries times 1/2 give bitwise identical results."""
+    k, q = _rand_slice(31, 80, 32, 3, 8, dtype="f32")
+    a = oracle.slice_eval(k, q, budget=40)
+    b = oracle.slice_eval(k * np.float32(2.0), q * np.float32(0.5), budget=40)
+    for name in ("importance", "rowmean", "counts", "rbar", "R", "Z", "keep"):
+        assert np.array_equal(getattr(a, name), getattr(b, name)), name
+
+
+def check_budget_invariants():
+    """|keep| = min(N, B); the window is kept; keep is strictly ascending with keep[j] >= j."""
+    rng = np.random.default_rng(3)
+    for trial in range(60):
+        n = int(rng.integers(2, 64))
+        alpha = int(rng.integers(1, 9))
+        budget = int(rng.integers(alpha + 1, alpha + 40))
+        g = int(rng.integers(1, 4))
+        k, q = _rand_slice(1000 + trial, n, 16, g, alpha)
+        r = oracle.slice_eval(k, q, budget=budget, obs_window=alpha, beta=int(rng.integers(0, 4)))
+        keep = r.keep
+        assert r.kept == len(keep) == min(n, budget)
+        assert np.all(np.diff(keep) > 0)
+        assert np.all(keep >= np.arange(len(keep)))
+        if n > budget:
+            assert set(range(n - alpha, n)) <= set(keep.tolist())
+
+
+def check_bruteforce_topk():
+    """Tiny slices: the chosen candidates maximise sum(Z) over every k-subset,
+    and no excluded candidate beats an included one (ties: newer wins)."""
+    for trial in range(12):
+        rng = np.random.default_rng(2000 + trial)
+        n = int(rng.integers(7, 13))
+        alpha = 2
+        budget = int(rng.integers(3, n))
+        k, q = _rand_slice(3000 + trial, n, 8, 2, alpha)
+        if trial % 3 == 0:
+            k[3] = k[1]  # an exact duplicate pair
+        r = oracle.slice_eval(k, q, budget=budget, obs_window=alpha, beta=1)
+        nc, kk = n - alpha, budget - alpha
+        chosen = [i for i in r.keep if i < nc]
+        best = max(sum(r.Z[list(s)]) for s in itertools.combinations(range(nc), kk))
+        assert abs(sum(r.Z[chosen]) - best) < 1e-15
+        for c in range(nc):
+            if c in chosen:
+                continue
+            for s in chosen:
+                assert r.Z[s] > r.Z[c] or (r.Z[s] == r.Z[c] and s > c)
+
+
+def check_lambda0_least_redundant():
+    """lambda = 0: Z = -R, so the k least redundant candidates are kept."""
+    k, q = _rand_slice(44, 60, 16, 2, 4)
+    kf = synth.to_float(k, "bf16").astype(np.float32)
+    for i in range(10, 40, 3):  # near-duplicates of earlier keys make redundancy spread out
+        kf[i] = kf[i - 7] + np.float32(0.01) * kf[i]
+    r = oracle.slice_eval(kf, synth.to_float(q, "bf16").astype(np.float32), budget=30, obs_window=4, beta=1,
+                          lam=0.0)
+    nc = 56
+    order = sorted(range(nc), key=lambda i: (r.rbar[i], -i))
+    assert list(r.keep) == sorted(order[:26] + list(range(nc, 60)))
+
+
+def check_step_noop_and_compaction():
+    """The whole step: a no-op below the trigger; above it, every slice's kept
+    rows land in order in [B - kept, B), bitwise equal to the source rows."""
+    w = synth.small(num_layers=2, batch=3, num_kv_heads=2, group=2, budget=96, buffer=32,
+                    lengths=("uniform", 60, 128), span_len=16, extra_capacity=8)
+    c = synth.build_cache(w, seed=1)
+    # below the trigger: nothing changes
+    K0, V0, s0 = c.K.copy(), c.V.copy(), c.seq_start.copy()
+    ev, ns, _ = oracle.evict_step(K0, V0, c.Q, s0, w.n_slots - 1, w.budget, w.buffer)
+    assert not ev and ns == w.n_slots - 1
+    assert np.array_equal(K0.view(np.uint8), c.K.view(np.uint8)) and np.array_equal(s0, c.seq_start)
+    K1, V1, s1 = c.K.copy(), c.V.copy(), c.seq_start.copy()
+    ev, ns, keep = oracle.evict_step(K1, V1, c.Q, s1, w.n_slots, w.budget, w.buffer)
+    assert ev and ns == w.budget
+    B = w.budget
+    for l in range(w.num_layers):
+        for b in range(w.batch):
+            n = int(c.lengths[b])
+            kept = min(n, B)
+            assert s1[b] == B - kept
+            for h in range(w.num_kv_heads):
+                kr = keep[l, b, h]
+                assert np.all(kr[: B - kept] == -1)
+                src = kr[B - kept:]
+                ref = oracle.slice_eval(c.K[l, b, h, c.seq_start[b]:w.n_slots],
+                                        c.Q[l, b, h * w.group:(h + 1) * w.group], budget=B)
+                assert np.array_equal(src, ref.keep + c.seq_start[b])
+                assert np.array_equal(K1[l, b, h, B - kept:B], c.K[l, b, h][src])  # numpy fancy-index gather
+                assert np.array_equal(V1[l, b, h, B - kept:B], c.V[l, b, h][src])
+                # canary rows past n_slots are untouched
+                assert np.array_equal(K1[l, b, h, w.n_slots:].view(np.uint16), c.K[l, b, h, w.n_slots:].view(np.uint16))
+
+
+ALL_CHECKS = [
+    check_hand_cases,
+    check_lambda1_textbook,
+    check_single_query_softmax,
+    check_probability_sums,
+    check_rowmean_identity,
+    check_exact_duplicates,
+    check_orthogonal_keys,
+    check_scale_invariance,
+    check_budget_invariants,
+    check_bruteforce_topk,
+    check_lambda0_least_redundant,
+    check_step_noop_and_compaction,
+]
