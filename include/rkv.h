@@ -1,0 +1,174 @@
+/*
+ * librkv — decode-time R-KV KV-cache eviction on AMD Instinct MI355X (gfx950).
+ *
+ * R-KV (redundancy-aware KV-cache compression for reasoning models) keeps a
+ * fixed-budget KV cache during decoding. Every time budget + buffer slots are
+ * full it keeps the newest observation tokens, scores every other cached
+ * token by importance (observation-query attention, max-pooled over the
+ * query heads of a GQA group) and by redundancy (cosine similarity of its key
+ * to the other keys of the same head, with the most recent similar tokens
+ * protected), combines the two and keeps the top tokens up to the budget.
+ * Source: R-KV notes page (yoonschallenge.tistory.com/1236), opening notes,
+ * summary table rows "decoding-time compression", "importance computation",
+ * "redundancy computation", "final selection criterion", and Q&A part 2,
+ * cause 3 (the per-128-token compression work).
+ *
+ * Readings where the page is silent (stated, not printed on the page):
+ *   Z_i = lambda*I_i - (1-lambda)*R_i with R = softmax of the redundancy over
+ *   the candidates; "similar" means cosine > sim_threshold; token i is
+ *   protected (redundancy 0) iff fewer than beta newer tokens are similar to
+ *   it; otherwise its redundancy is its mean cosine to the other N-1 valid
+ *   tokens; the budget includes the observation window; equal scores go to
+ *   the newer token; each (layer, sequence, KV head) selects independently.
+ *
+ * CONVENTIONS (every entry point)
+ *   Memory. Every pointer is a DEVICE pointer unless marked HOST. The caller
+ *   owns all memory; the library never allocates or frees device memory and
+ *   keeps no state between calls except a thread-local last HIP error.
+ *   Layout. Per-layer caches K and V are [batch][num_kv_heads][capacity]
+ *   [head_dim] rows, contiguous (row stride head_dim elements), 16-byte
+ *   aligned. Sequence b holds N_b = n_slots - seq_start[b] valid tokens in
+ *   slots [seq_start[b], n_slots) (left padding); padding slots are never
+ *   read. obs_q is [num_layers][batch][num_kv_heads*group][obs_window]
+ *   [head_dim], same element type; query head hq belongs to KV head
+ *   hq / group; row t of a head is the query of token N_b - obs_window + t.
+ *   Score arrays are float32 [num_layers][batch][num_kv_heads][n_slots]
+ *   indexed by slot; keep is int32 [num_layers][batch][num_kv_heads][budget].
+ *   Streams. `stream` is a hipStream_t (NULL = the null stream). Work is
+ *   enqueued asynchronously; no entry point synchronises the host.
+ *   Errors. Arguments are validated on the host before anything is
+ *   enqueued; on any error nothing is launched and nothing is written.
+ *   A failed launch returns RKV_ERR_HIP (see rkv_last_hip_error). Device
+ *   data preconditions (0 <= seq_start[b] <= n_slots, finite values in valid
+ *   slots) cannot be checked without a host sync: the kernels clamp
+ *   seq_start into range so a violation never addresses memory outside the
+ *   caller's buffers, but the result is then unspecified. No entry point
+ *   prints, aborts or throws.
+ */
+#ifndef RKV_H
+#define RKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RKV_OK = 0,
+  RKV_ERR_NULL_ARG = 1,            /* a required pointer is NULL                      */
+  RKV_ERR_BAD_SHAPE = 2,           /* sizes out of range or inconsistent              */
+  RKV_ERR_BAD_PARAM = 3,           /* lambda, sim_threshold, beta or dtype invalid    */
+  RKV_ERR_WORKSPACE_TOO_SMALL = 4, /* ws_bytes < rkv_workspace_bytes(p)               */
+  RKV_ERR_MISALIGNED = 5,          /* a tensor pointer is not 16-byte aligned         */
+  RKV_ERR_UNSUPPORTED = 6,         /* valid but not implemented (e.g. head_dim != 128) */
+  RKV_ERR_HIP = 7                  /* a HIP launch failed                             */
+} rkv_status;
+
+typedef enum { RKV_BF16 = 0, RKV_F32 = 1 } rkv_dtype;
+
+#define RKV_MAX_LAYERS 128     /* per-layer pointers travel by value in kernel arguments */
+#define RKV_MAX_CAPACITY 16384 /* slots per (sequence, head) row block                   */
+#define RKV_MAX_QROWS 64       /* group * obs_window                                     */
+
+typedef struct {
+  int32_t num_layers;   /* L, 1..RKV_MAX_LAYERS                                     */
+  int32_t batch;        /* sequences per layer tensor, >= 1                         */
+  int32_t num_kv_heads; /* KV heads, >= 1                                           */
+  int32_t group;        /* query heads per KV head (GQA group), >= 1                */
+  int32_t head_dim;     /* D; 128 is the only supported value                       */
+  int32_t capacity;     /* slots per (sequence, head); >= budget + buffer           */
+  int32_t budget;       /* B: tokens kept per (sequence, head), window included     */
+  int32_t buffer;       /* new tokens between evictions (R-KV default 128), >= 1    */
+  int32_t obs_window;   /* alpha: observation tokens (R-KV default 8), 1..budget-1  */
+  int32_t beta;         /* protection count, >= 0                                   */
+  float lambda;         /* importance weight in [0, 1] (R-KV best: 0.1)             */
+  float sim_threshold;  /* tau in [-1, 1]                                           */
+  int32_t dtype;        /* rkv_dtype of K, V and obs_q                              */
+} rkv_params;
+
+/* Bytes of device workspace rkv_score and rkv_evict_step need for p (sized
+ * for n_slots = capacity); 0 if p is invalid. Any 256-byte-aligned buffer of
+ * at least this size works; its content need not be initialised and is
+ * clobbered. */
+size_t rkv_workspace_bytes(const rkv_params* p);
+
+/*
+ * Importance and redundancy of every valid token of every (layer, sequence,
+ * KV head) whose sequence has outgrown the budget (N_b > budget); other
+ * sequences' entries are left unchanged.
+ *   k_layers   HOST array of num_layers device pointers to K caches (read only)
+ *   obs_q      observation queries (read only)
+ *   seq_start  [batch] int32 first valid slot per sequence (read only)
+ *   n_slots    slots in use, budget < n_slots <= capacity is the useful range,
+ *              0 <= n_slots <= capacity is accepted
+ *   importance out: I_j = max over the group's query heads of the mean over
+ *              the obs_window queries of the causal softmax attention weight
+ *              on key j (scale 1/sqrt(head_dim))
+ *   redundancy out: rbar_j = 0 if protected, else mean cosine of key j to the
+ *              other N_b - 1 valid keys
+ *   counts     out, nullable: int32 c_j = #{ newer valid tokens with cosine >
+ *              sim_threshold }
+ *   ws, ws_bytes  workspace (see rkv_workspace_bytes)
+ */
+rkv_status rkv_score(const rkv_params* p, const void* const* k_layers, const void* obs_q, const int32_t* seq_start,
+                     int32_t n_slots, float* importance, float* redundancy, int32_t* counts, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/*
+ * Selection from given scores. For each (layer, sequence, KV head) with
+ * N_b > budget: R = softmax of redundancy over the candidates (the N_b -
+ * obs_window oldest valid tokens), Z = lambda*I - (1-lambda)*R, the
+ * budget - obs_window candidates with the largest Z (equal Z: the later slot
+ * wins) plus the obs_window newest tokens are kept. With N_b <= budget every
+ * valid token is kept. keep[j] receives the source slot of destination slot
+ * j in ascending order, right-aligned: entries [0, budget - kept) are -1.
+ * keep[j] >= j always holds.
+ *   importance, redundancy  score arrays (read only)
+ *   seq_start  read only; budget <= n_slots <= capacity
+ *   keep       out
+ *   z_out, r_out  out, nullable: Z and R at candidate slots of evicting
+ *              sequences (other entries unchanged)
+ */
+rkv_status rkv_select(const rkv_params* p, const float* importance, const float* redundancy,
+                      const int32_t* seq_start, int32_t n_slots, int32_t* keep, float* z_out, float* r_out,
+                      void* stream);
+
+/*
+ * In-place, order-preserving compaction: for every (layer, sequence, KV
+ * head) row j of K and V in [0, budget) with keep[j] >= 0 receives the bytes
+ * of row keep[j]; then seq_start[b] = number of -1 entries of the sequence's
+ * keep rows. Rows with keep[j] = -1 and rows >= budget are left as they are.
+ *   k_layers, v_layers  HOST arrays of num_layers device pointers (modified)
+ *   keep       as produced by rkv_select (ascending, keep[j] >= j required)
+ *   seq_start  in/out; budget <= n_slots <= capacity
+ */
+rkv_status rkv_compact(const rkv_params* p, void* const* k_layers, void* const* v_layers, const int32_t* keep,
+                       int32_t* seq_start, int32_t n_slots, void* stream);
+
+/*
+ * One decode-time eviction step over all layers, sequences and KV heads.
+ * If *n_slots < budget + buffer nothing is launched or written (RKV_OK).
+ * Otherwise scoring, selection and compaction run on `stream` and *n_slots
+ * becomes budget; afterwards sequence b holds min(N_b, budget) tokens in
+ * slots [seq_start[b], budget), in their original order.
+ *   k_layers, v_layers  HOST arrays of device pointers (modified in place)
+ *   obs_q      observation queries (read only)
+ *   seq_start  in/out
+ *   n_slots    HOST in/out
+ *   ws, ws_bytes  workspace (see rkv_workspace_bytes)
+ */
+rkv_status rkv_evict_step(const rkv_params* p, void* const* k_layers, void* const* v_layers, const void* obs_q,
+                          int32_t* seq_start, int32_t* n_slots, void* ws, size_t ws_bytes, void* stream);
+
+/* Static string naming a status. */
+const char* rkv_status_string(rkv_status st);
+
+/* hipError_t of the last failed launch on this thread (0 if none). */
+int rkv_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RKV_H */

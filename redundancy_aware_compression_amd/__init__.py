@@ -1,0 +1,31 @@
+"""R-KV decode-time KV-cache eviction on AMD Instinct MI355X (gfx950).
+
+The work happens in ``librkv.so`` (hand-written HIP kernels behind a C ABI,
+declared in ``include/rkv.h``). This module only marshals arguments to it with
+ctypes; it has no compute of its own and no fallback: importing it fails
+loudly when the library has not been built.
+
+Pointers may be given as integers or as objects with ``data_ptr()`` (torch
+tensors). ``stream`` defaults to torch's current HIP stream.
+"""
+from __future__ import annotations
+
+from ._binding import (  # noqa: F401
+    RKV_BF16,
+    RKV_F32,
+    RKV_MAX_CAPACITY,
+    RKV_MAX_LAYERS,
+    RKV_MAX_QROWS,
+    STATUS,
+    RkvError,
+    RkvParams,
+    library_path,
+    make_params,
+    rkv_compact,
+    rkv_evict_step,
+    rkv_last_hip_error,
+    rkv_score,
+    rkv_select,
+    rkv_status_string,
+    rkv_workspace_bytes,
+)

@@ -1,0 +1,169 @@
+"""ctypes marshalling for librkv.so; names and argument order follow include/rkv.h."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = os.path.join(_HERE, "librkv.so")
+
+RKV_BF16 = 0
+RKV_F32 = 1
+RKV_MAX_LAYERS = 128
+RKV_MAX_CAPACITY = 16384
+RKV_MAX_QROWS = 64
+
+STATUS = {
+    0: "RKV_OK",
+    1: "RKV_ERR_NULL_ARG",
+    2: "RKV_ERR_BAD_SHAPE",
+    3: "RKV_ERR_BAD_PARAM",
+    4: "RKV_ERR_WORKSPACE_TOO_SMALL",
+    5: "RKV_ERR_MISALIGNED",
+    6: "RKV_ERR_UNSUPPORTED",
+    7: "RKV_ERR_HIP",
+}
+
+
+class RkvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {STATUS.get(status, status)}"
+        if status == 7:
+            msg += f" (hipError {_lib().rkv_last_hip_error()})"
+        super().__init__(msg)
+
+
+class RkvParams(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("capacity", ctypes.c_int32),
+        ("budget", ctypes.c_int32),
+        ("buffer", ctypes.c_int32),
+        ("obs_window", ctypes.c_int32),
+        ("beta", ctypes.c_int32),
+        ("lambda_", ctypes.c_float),
+        ("sim_threshold", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+def make_params(num_layers: int, batch: int, num_kv_heads: int, group: int, capacity: int, budget: int,
+                buffer: int = 128, obs_window: int = 8, beta: int = 2, lam: float = 0.1, tau: float = 0.5,
+                dtype: str = "bf16", head_dim: int = 128) -> RkvParams:
+    code = {"bf16": RKV_BF16, "f32": RKV_F32}[dtype] if isinstance(dtype, str) else int(dtype)
+    return RkvParams(num_layers, batch, num_kv_heads, group, head_dim, capacity, budget, buffer, obs_window, beta,
+                     lam, tau, code)
+
+
+_handle = None
+
+
+def library_path() -> str:
+    return _LIB
+
+
+def _lib():
+    global _handle
+    if _handle is None:
+        if not os.path.exists(_LIB):
+            raise ImportError(f"librkv.so is not built at {_LIB}; run `python -m redundancy_aware_compression_amd.build`")
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.POINTER(RkvParams)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.rkv_workspace_bytes.restype = sz
+        L.rkv_workspace_bytes.argtypes = [P]
+        L.rkv_score.restype = ctypes.c_int
+        L.rkv_score.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+        L.rkv_select.restype = ctypes.c_int
+        L.rkv_select.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp]
+        L.rkv_compact.restype = ctypes.c_int
+        L.rkv_compact.argtypes = [P, vp, vp, vp, vp, i32, vp]
+        L.rkv_evict_step.restype = ctypes.c_int
+        L.rkv_evict_step.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(i32), vp, sz, vp]
+        L.rkv_status_string.restype = ctypes.c_char_p
+        L.rkv_status_string.argtypes = [ctypes.c_int]
+        L.rkv_last_hip_error.restype = ctypes.c_int
+        L.rkv_last_hip_error.argtypes = []
+        _handle = L
+    return _handle
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _ptr_array(xs: Sequence) -> ctypes.Array:
+    return (ctypes.c_void_p * len(xs))(*[_ptr(x) for x in xs])
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+
+        return int(torch.cuda.current_stream().cuda_stream) if torch.cuda.is_available() else None
+    if isinstance(stream, int):
+        return stream
+    return int(stream.cuda_stream)
+
+
+def _check(st: int, where: str) -> int:
+    if st != 0:
+        raise RkvError(st, where)
+    return st
+
+
+def rkv_workspace_bytes(p: RkvParams) -> int:
+    return int(_lib().rkv_workspace_bytes(ctypes.byref(p)))
+
+
+def rkv_status_string(st: int) -> str:
+    return _lib().rkv_status_string(st).decode()
+
+
+def rkv_last_hip_error() -> int:
+    return int(_lib().rkv_last_hip_error())
+
+
+def rkv_score(p: RkvParams, k_layers: Sequence, obs_q, seq_start, n_slots: int, importance, redundancy,
+              counts=None, ws=None, ws_bytes: int = 0, stream=None, check: bool = True) -> int:
+    st = _lib().rkv_score(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p), _ptr(obs_q),
+                          _ptr(seq_start), n_slots, _ptr(importance), _ptr(redundancy), _ptr(counts), _ptr(ws),
+                          ws_bytes, _stream(stream))
+    return _check(st, "rkv_score") if check else st
+
+
+def rkv_select(p: RkvParams, importance, redundancy, seq_start, n_slots: int, keep, z_out=None, r_out=None,
+               stream=None, check: bool = True) -> int:
+    st = _lib().rkv_select(ctypes.byref(p), _ptr(importance), _ptr(redundancy), _ptr(seq_start), n_slots, _ptr(keep),
+                           _ptr(z_out), _ptr(r_out), _stream(stream))
+    return _check(st, "rkv_select") if check else st
+
+
+def rkv_compact(p: RkvParams, k_layers: Sequence, v_layers: Sequence, keep, seq_start, n_slots: int, stream=None,
+                check: bool = True) -> int:
+    st = _lib().rkv_compact(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
+                            ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(keep), _ptr(seq_start), n_slots,
+                            _stream(stream))
+    return _check(st, "rkv_compact") if check else st
+
+
+def rkv_evict_step(p: RkvParams, k_layers: Sequence, v_layers: Sequence, obs_q, seq_start, n_slots: int, ws,
+                   ws_bytes: int, stream=None, check: bool = True):
+    """Returns (status, n_slots after the step)."""
+    ns = ctypes.c_int32(n_slots)
+    st = _lib().rkv_evict_step(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
+                               ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(obs_q), _ptr(seq_start),
+                               ctypes.byref(ns), _ptr(ws), ws_bytes, _stream(stream))
+    if check:
+        _check(st, "rkv_evict_step")
+    return st, ns.value

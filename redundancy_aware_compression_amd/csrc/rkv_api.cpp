@@ -1,0 +1,181 @@
+// librkv C ABI: argument validation, workspace carving and kernel sequencing.
+// Validation runs entirely on the host before anything is enqueued, so every
+// error path leaves device memory untouched and needs no GPU.
+#include <string.h>
+
+#include "rkv.h"
+#include "rkv_internal.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+rkv_status check_params(const rkv_params* p) {
+  if (!p) return RKV_ERR_NULL_ARG;
+  if (p->dtype != RKV_BF16 && p->dtype != RKV_F32) return RKV_ERR_BAD_PARAM;
+  if (!(p->lambda >= 0.f && p->lambda <= 1.f)) return RKV_ERR_BAD_PARAM;
+  if (!(p->sim_threshold >= -1.f && p->sim_threshold <= 1.f)) return RKV_ERR_BAD_PARAM;
+  if (p->beta < 0) return RKV_ERR_BAD_PARAM;
+  if (p->num_layers < 1 || p->num_layers > RKV_MAX_LAYERS) return RKV_ERR_BAD_SHAPE;
+  if (p->batch < 1 || p->num_kv_heads < 1 || p->group < 1) return RKV_ERR_BAD_SHAPE;
+  if (p->obs_window < 1 || p->budget <= p->obs_window || p->buffer < 1) return RKV_ERR_BAD_SHAPE;
+  if (p->head_dim < 1) return RKV_ERR_BAD_SHAPE;
+  if ((int64_t)p->budget + p->buffer > p->capacity) return RKV_ERR_BAD_SHAPE;
+  if (p->capacity > RKV_MAX_CAPACITY) return RKV_ERR_UNSUPPORTED;
+  if (p->head_dim != rkv::kHeadDim) return RKV_ERR_UNSUPPORTED;
+  if ((int64_t)p->group * p->obs_window > RKV_MAX_QROWS) return RKV_ERR_UNSUPPORTED;
+  // slices index a 1-D grid (times the per-slice work units) and 2-D grids' y
+  const int64_t slices = (int64_t)p->num_layers * p->batch * p->num_kv_heads;
+  if (slices > 65535) return RKV_ERR_UNSUPPORTED;
+  if (slices * rkv::gram_units(p->capacity) > 0x7FFFFFFF) return RKV_ERR_UNSUPPORTED;
+  return RKV_OK;
+}
+
+rkv_status check_layers(const rkv_params* p, const void* const* layers) {
+  if (!layers) return RKV_ERR_NULL_ARG;
+  for (int l = 0; l < p->num_layers; ++l) {
+    if (!layers[l]) return RKV_ERR_NULL_ARG;
+    if (!aligned16(layers[l])) return RKV_ERR_MISALIGNED;
+  }
+  return RKV_OK;
+}
+
+rkv::Geom make_geom(const rkv_params* p, int32_t n_slots) {
+  rkv::Geom g;
+  g.L = p->num_layers;
+  g.batch = p->batch;
+  g.H = p->num_kv_heads;
+  g.G = p->group;
+  g.capacity = p->capacity;
+  g.budget = p->budget;
+  g.alpha = p->obs_window;
+  g.beta = p->beta;
+  g.n_slots = n_slots;
+  g.qrows = p->group * p->obs_window;
+  g.lambda = p->lambda;
+  g.tau = p->sim_threshold;
+  return g;
+}
+
+rkv::LayerPtrs make_layers(const rkv_params* p, const void* const* layers) {
+  rkv::LayerPtrs lp;
+  memset(&lp, 0, sizeof(lp));
+  for (int l = 0; l < p->num_layers; ++l) lp.p[l] = layers[l];
+  return lp;
+}
+
+rkv_status hip_status(int err) {
+  if (err == 0) return RKV_OK;
+  g_last_hip_error = err;
+  return RKV_ERR_HIP;
+}
+
+#define RKV_TRY(x)                         \
+  do {                                     \
+    rkv_status st_ = hip_status((x));      \
+    if (st_ != RKV_OK) return st_;         \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t rkv_workspace_bytes(const rkv_params* p) {
+  if (check_params(p) != RKV_OK) return 0;
+  return rkv::carve(*p, nullptr).bytes;
+}
+
+const char* rkv_status_string(rkv_status st) {
+  switch (st) {
+    case RKV_OK: return "RKV_OK";
+    case RKV_ERR_NULL_ARG: return "RKV_ERR_NULL_ARG";
+    case RKV_ERR_BAD_SHAPE: return "RKV_ERR_BAD_SHAPE";
+    case RKV_ERR_BAD_PARAM: return "RKV_ERR_BAD_PARAM";
+    case RKV_ERR_WORKSPACE_TOO_SMALL: return "RKV_ERR_WORKSPACE_TOO_SMALL";
+    case RKV_ERR_MISALIGNED: return "RKV_ERR_MISALIGNED";
+    case RKV_ERR_UNSUPPORTED: return "RKV_ERR_UNSUPPORTED";
+    case RKV_ERR_HIP: return "RKV_ERR_HIP";
+  }
+  return "RKV_ERR_UNKNOWN";
+}
+
+int rkv_last_hip_error(void) { return g_last_hip_error; }
+
+rkv_status rkv_score(const rkv_params* p, const void* const* k_layers, const void* obs_q, const int32_t* seq_start,
+                     int32_t n_slots, float* importance, float* redundancy, int32_t* counts, void* ws,
+                     size_t ws_bytes, void* stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  if ((st = check_layers(p, k_layers)) != RKV_OK) return st;
+  if (!obs_q || !seq_start || !importance || !redundancy || !ws) return RKV_ERR_NULL_ARG;
+  if (!aligned16(obs_q) || ((uintptr_t)ws & 255u)) return RKV_ERR_MISALIGNED;
+  if (n_slots < 0 || n_slots > p->capacity) return RKV_ERR_BAD_SHAPE;
+  rkv::Workspace w = rkv::carve(*p, ws);
+  if (ws_bytes < w.bytes) return RKV_ERR_WORKSPACE_TOO_SMALL;
+  if (n_slots <= p->budget) return RKV_OK;  // no sequence can exceed the budget
+  const rkv::Geom g = make_geom(p, n_slots);
+  const rkv::LayerPtrs kl = make_layers(p, k_layers);
+  int32_t* cnt = counts ? counts : w.counts;
+  RKV_TRY(rkv::launch_stats(g, p->dtype, kl, obs_q, seq_start, w.norms, cnt, w.stats, w.ssum, stream));
+  RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, w.norms, w.stats, w.ssum, importance, w.rowmean, cnt,
+                           stream));
+  RKV_TRY(rkv::launch_redundancy(g, seq_start, cnt, w.rowmean, redundancy, stream));
+  return RKV_OK;
+}
+
+rkv_status rkv_select(const rkv_params* p, const float* importance, const float* redundancy,
+                      const int32_t* seq_start, int32_t n_slots, int32_t* keep, float* z_out, float* r_out,
+                      void* stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  if (!importance || !redundancy || !seq_start || !keep) return RKV_ERR_NULL_ARG;
+  if (n_slots < p->budget || n_slots > p->capacity) return RKV_ERR_BAD_SHAPE;
+  const rkv::Geom g = make_geom(p, n_slots);
+  RKV_TRY(rkv::launch_select(g, importance, redundancy, nullptr, nullptr, seq_start, keep, z_out, r_out, stream));
+  return RKV_OK;
+}
+
+rkv_status rkv_compact(const rkv_params* p, void* const* k_layers, void* const* v_layers, const int32_t* keep,
+                       int32_t* seq_start, int32_t n_slots, void* stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  if ((st = check_layers(p, (const void* const*)k_layers)) != RKV_OK) return st;
+  if ((st = check_layers(p, (const void* const*)v_layers)) != RKV_OK) return st;
+  if (!keep || !seq_start) return RKV_ERR_NULL_ARG;
+  if (n_slots < p->budget || n_slots > p->capacity) return RKV_ERR_BAD_SHAPE;
+  const rkv::Geom g = make_geom(p, n_slots);
+  RKV_TRY(rkv::launch_compact(g, p->dtype, make_layers(p, (const void* const*)k_layers),
+                              make_layers(p, (const void* const*)v_layers), keep, seq_start, stream));
+  return RKV_OK;
+}
+
+rkv_status rkv_evict_step(const rkv_params* p, void* const* k_layers, void* const* v_layers, const void* obs_q,
+                          int32_t* seq_start, int32_t* n_slots, void* ws, size_t ws_bytes, void* stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  if ((st = check_layers(p, (const void* const*)k_layers)) != RKV_OK) return st;
+  if ((st = check_layers(p, (const void* const*)v_layers)) != RKV_OK) return st;
+  if (!obs_q || !seq_start || !n_slots || !ws) return RKV_ERR_NULL_ARG;
+  if (!aligned16(obs_q) || ((uintptr_t)ws & 255u)) return RKV_ERR_MISALIGNED;
+  const int32_t ns = *n_slots;
+  if (ns < 0 || ns > p->capacity) return RKV_ERR_BAD_SHAPE;
+  rkv::Workspace w = rkv::carve(*p, ws);
+  if (ws_bytes < w.bytes) return RKV_ERR_WORKSPACE_TOO_SMALL;
+  // R-KV compresses once budget + buffer slots are full; below that, no-op.
+  if (ns < p->budget + p->buffer) return RKV_OK;
+  const rkv::Geom g = make_geom(p, ns);
+  const rkv::LayerPtrs kl = make_layers(p, (const void* const*)k_layers);
+  const rkv::LayerPtrs vl = make_layers(p, (const void* const*)v_layers);
+  RKV_TRY(rkv::launch_stats(g, p->dtype, kl, obs_q, seq_start, w.norms, w.counts, w.stats, w.ssum, stream));
+  RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, w.norms, w.stats, w.ssum, w.importance, w.rowmean,
+                           w.counts, stream));
+  RKV_TRY(rkv::launch_select(g, w.importance, nullptr, w.counts, w.rowmean, seq_start, w.keep, nullptr, nullptr,
+                             stream));
+  RKV_TRY(rkv::launch_compact(g, p->dtype, kl, vl, w.keep, seq_start, stream));
+  *n_slots = p->budget;
+  return RKV_OK;
+}
+
+}  // extern "C"

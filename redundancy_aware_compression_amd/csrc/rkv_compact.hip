@@ -1,0 +1,89 @@
+// K5 — in-place, order-preserving compaction of the kept K/V rows.
+//
+// R-KV notes page (yoonschallenge.tistory.com/1236), Q&A part 2, cause 3: the
+// selected KV is copied into the new cache; cause 4 lists the costs this
+// avoids — re-allocation and re-arrangement of KV tensors after pruning. The
+// cache is compacted where it lies: row j of [0, budget) receives row keep[j].
+//
+// Safety of the in-place gather: keep is ascending with keep[j] >= j, so when
+// destinations are processed in ascending chunks, a chunk's writes land below
+// every source of every later chunk, and its own sources are all read before
+// any of its writes (loads, a full vmcnt wait, then a barrier, then stores).
+// One work-group therefore owns one (slice, K|V) row block; different
+// work-groups touch disjoint memory. Rows with keep[j] == j are skipped.
+#include "rkv_device.hpp"
+
+namespace rkv {
+
+constexpr int kCompactThreads = 256;
+constexpr int kCompactUnroll = 8;  // 16-byte loads in flight per thread per chunk
+
+template <typename T>
+__global__ __launch_bounds__(kCompactThreads) void compact_kernel(Geom g, LayerPtrs k, LayerPtrs v,
+                                                                  const int32_t* __restrict__ keep,
+                                                                  int32_t* __restrict__ seq_start) {
+  constexpr int RB = kHeadDim * Elem<T>::kBytes;
+  constexpr int U4_ROW = RB / 16;
+  constexpr int CH_ROWS = kCompactThreads * kCompactUnroll / U4_ROW;
+
+  const int wid = xcd_remap(blockIdx.x, gridDim.x);
+  const int slice = wid >> 1, kv = wid & 1;
+  int l, b, h;
+  slice_coords(g, slice, l, b, h);
+  char* base = (char*)(kv ? v.p[l] : k.p[l]) + ((size_t)b * g.H + h) * g.capacity * (size_t)RB;
+  const int32_t* krow = keep + (size_t)slice * g.budget;
+  const int B = g.budget, tid = threadIdx.x;
+
+  if (kv == 0 && l == 0 && h == 0 && tid == 0) {
+    // new first valid slot = number of leading -1 entries (binary search)
+    int lo = 0, hi = B;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (krow[mid] < 0) lo = mid + 1; else hi = mid;
+    }
+    seq_start[b] = lo;
+  }
+
+  // Eight 16-byte loads per thread per chunk, held in named registers (an
+  // array here is kept in scratch memory across the barrier by the compiler).
+  static_assert(kCompactUnroll == 8, "the chunk body below is written out for 8 loads");
+  for (int c0 = 0; c0 < B; c0 += CH_ROWS) {
+    uint4 v0, v1, v2, v3, v4, v5, v6, v7;
+    uint32_t mvmask = 0;
+    auto ld = [&](int q, uint4& val) {
+      const int idx = q * kCompactThreads + tid;
+      const int jr = c0 + idx / U4_ROW;
+      const int j = min(jr, B - 1), part = idx % U4_ROW;
+      const int src = krow[j];
+      const bool mv = jr < B && src >= 0 && src != j && src < g.n_slots;  // out-of-range sources are ignored
+      mvmask |= (uint32_t)mv << q;
+      // rows that stay put load their own (in-bounds) bytes and store nothing
+      val = *(const uint4*)(base + (size_t)(mv ? src : j) * RB + part * 16);
+    };
+    ld(0, v0); ld(1, v1); ld(2, v2); ld(3, v3); ld(4, v4); ld(5, v5); ld(6, v6); ld(7, v7);
+    // every source of this chunk is in registers before any row is overwritten
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    auto st = [&](int q, const uint4& val) {
+      const int idx = q * kCompactThreads + tid;
+      if ((mvmask >> q) & 1u) *(uint4*)(base + (size_t)(c0 + idx / U4_ROW) * RB + (idx % U4_ROW) * 16) = val;
+    };
+    st(0, v0); st(1, v1); st(2, v2); st(3, v3); st(4, v4); st(5, v5); st(6, v6); st(7, v7);
+  }
+}
+
+int launch_compact(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const int32_t* keep,
+                   int32_t* seq_start, void* stream) {
+  const int slices = g.L * g.batch * g.H;
+  if (slices == 0) return 0;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == RKV_BF16)
+    hipLaunchKernelGGL(compact_kernel<bf16_t>, dim3(2 * slices), dim3(kCompactThreads), 0, s, g, k, v, keep,
+                       seq_start);
+  else
+    hipLaunchKernelGGL(compact_kernel<float>, dim3(2 * slices), dim3(kCompactThreads), 0, s, g, k, v, keep,
+                       seq_start);
+  return (int)hipGetLastError();
+}
+
+}  // namespace rkv

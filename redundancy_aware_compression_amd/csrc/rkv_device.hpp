@@ -1,0 +1,181 @@
+// Device-side building blocks of the gfx950 kernels: element types, key
+// fragments in the MFMA operand layout, wave/block reductions and the
+// XCD-aware work-group remap.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "rkv_internal.hpp"
+
+namespace rkv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Storage types: bf16 values travel as raw 16-bit patterns.
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<bf16_t> {
+  static constexpr int kBytes = 2;
+};
+template <>
+struct Elem<float> {
+  static constexpr int kBytes = 4;
+};
+
+// One lane's half of a key row in the 32x32 MFMA operand layout: lane l holds
+// dims [64*(l/32), 64*(l/32)+64) of key/query row (l % 32). Within a k-step
+// the hardware pairs operand lanes by l/32, so A and B fragments built the
+// same way contract the same dimension order; the order of the 128 dims is a
+// permutation of the dot product's terms.
+template <typename T>
+struct Frag {
+  static constexpr int kU4 = 64 * Elem<T>::kBytes / 16;  // 8 for bf16, 16 for f32
+  uint4 v[kU4];
+};
+
+__device__ inline float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// The 64 values of a fragment as fp32 (exact widening).
+template <typename T>
+__device__ inline float frag_val(const Frag<T>& f, int e);
+template <>
+__device__ inline float frag_val<bf16_t>(const Frag<bf16_t>& f, int e) {
+  const uint32_t w = ((const uint32_t*)&f.v[e >> 3])[(e & 7) >> 1];
+  return bf16_bits_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+template <>
+__device__ inline float frag_val<float>(const Frag<float>& f, int e) {
+  return __uint_as_float(((const uint32_t*)&f.v[e >> 2])[e & 3]);
+}
+
+template <typename T>
+__device__ inline void frag_zero(Frag<T>& f) {
+#pragma unroll
+  for (int i = 0; i < Frag<T>::kU4; ++i) f.v[i] = make_uint4(0, 0, 0, 0);
+}
+
+// Loads one lane's half row: `half_row` points at the lane's 64 values.
+template <typename T>
+__device__ inline void frag_load(Frag<T>& f, const void* half_row) {
+  const uint4* p = (const uint4*)half_row;
+#pragma unroll
+  for (int i = 0; i < Frag<T>::kU4; ++i) f.v[i] = p[i];
+}
+
+// acc += A-row fragment x B-column fragment over all 128 dims.
+__device__ inline void mma_frag(f32x16& acc, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a.v[s]),
+                                                  __builtin_bit_cast(bf16x8_t, b.v[s]), acc, 0, 0, 0);
+}
+__device__ inline void mma_frag(f32x16& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const float* x = (const float*)&a.v[s];
+    const float* y = (const float*)&b.v[s];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x[e], y[e], acc, 0, 0, 0);
+  }
+}
+
+// Row of the 32x32 MFMA result held in accumulator register r of a lane in
+// half `hh` (= lane / 32); the column is lane % 32.
+__device__ inline int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
+
+// Work-groups are dispatched round-robin over the 8 XCDs; remap the hardware
+// id so that consecutive logical work items share an XCD (and its L2).
+__device__ inline int xcd_remap(int bid, int nblocks) {
+  const int xcd = bid % kXcds, local = bid / kXcds;
+  const int per = nblocks / kXcds, rem = nblocks % kXcds;
+  return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+
+__device__ inline void slice_coords(const Geom& g, int slice, int& l, int& b, int& h) {
+  h = slice % g.H;
+  b = (slice / g.H) % g.batch;
+  l = slice / (g.H * g.batch);
+}
+
+// First valid slot and valid-token count of sequence b, with seq_start
+// clamped into [0, n_slots].
+__device__ inline void seq_range(const Geom& g, const int32_t* seq_start, int b, int& s0, int& N) {
+  int s = seq_start[b];
+  s = s < 0 ? 0 : (s > g.n_slots ? g.n_slots : s);
+  s0 = s;
+  N = g.n_slots - s;
+}
+
+template <typename T>
+__device__ inline const char* row_ptr(const void* layer, const Geom& g, int b, int h, int slot) {
+  return (const char*)layer + (((size_t)b * g.H + h) * g.capacity + slot) * (size_t)(kHeadDim * Elem<T>::kBytes);
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ inline int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Block-wide reductions (blockDim.x a multiple of 64, <= 1024); scratch holds
+// 16 values. Every thread receives the result.
+__device__ inline float block_max(float v, float* scratch) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[w] = v;
+  __syncthreads();
+  float r = scratch[0];
+  for (int i = 1; i < nw; ++i) r = fmaxf(r, scratch[i]);
+  return r;
+}
+__device__ inline float block_sum(float v, float* scratch) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) scratch[w] = v;
+  __syncthreads();
+  float r = 0.f;
+  for (int i = 0; i < nw; ++i) r += scratch[i];
+  return r;
+}
+
+// Exclusive prefix sum over the block in thread order; *total receives the
+// block total. scratch holds 16 ints.
+__device__ inline int block_exclusive_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) scratch[w] = x;
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    if (i < w) before += scratch[i];
+    tot += scratch[i];
+  }
+  *total = tot;
+  return before + x - v;
+}
+
+}  // namespace rkv

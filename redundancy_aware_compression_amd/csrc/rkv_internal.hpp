@@ -1,0 +1,118 @@
+// Internal definitions shared by the host layer and the gfx950 kernels of
+// librkv: kernel-argument blocks, workspace carving and the tiling constants.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "rkv.h"
+
+#if defined(__HIPCC__)
+#define RKV_HD __host__ __device__
+#else
+#define RKV_HD
+#endif
+
+namespace rkv {
+
+constexpr int kHeadDim = 128;    // D
+constexpr int kChunk = 128;      // keys per stats work-group
+constexpr int kColBlock = 128;   // Gram columns (older tokens) held in registers per work-group
+constexpr int kRowBlock = 64;    // Gram rows (newer tokens) staged in LDS per iteration
+constexpr int kSegBlocks = 6;    // row blocks per Gram work unit
+constexpr int kXcds = 8;         // MI355X accelerator complex dies
+
+// Geometry and method parameters common to every kernel.
+struct Geom {
+  int32_t L, batch, H, G, capacity, budget, alpha, beta;
+  int32_t n_slots;
+  int32_t qrows;   // G * alpha
+  float lambda, tau;
+};
+
+struct LayerPtrs {
+  const void* p[RKV_MAX_LAYERS];
+};
+
+// Gram work units of one slice with N valid tokens: column block I (kColBlock
+// older tokens) against row blocks of kRowBlock newer tokens starting at the
+// diagonal, split into segments of at most kSegBlocks row blocks.
+RKV_HD inline int gram_units(int N) {
+  int u = 0;
+  for (int i = 0; i * kColBlock < N; ++i) {
+    int nj = (N - i * kColBlock + kRowBlock - 1) / kRowBlock;
+    u += (nj + kSegBlocks - 1) / kSegBlocks;
+  }
+  return u;
+}
+
+RKV_HD inline bool gram_unit_of(int u, int N, int& I, int& jb_lo, int& jb_hi) {
+  for (int i = 0; i * kColBlock < N; ++i) {
+    int nj = (N - i * kColBlock + kRowBlock - 1) / kRowBlock;
+    int nseg = (nj + kSegBlocks - 1) / kSegBlocks;
+    if (u < nseg) {
+      I = i;
+      jb_lo = u * kSegBlocks;
+      jb_hi = jb_lo + kSegBlocks < nj ? jb_lo + kSegBlocks : nj;
+      return true;
+    }
+    u -= nseg;
+  }
+  return false;
+}
+
+RKV_HD inline int chunks_of(int n) { return (n + kChunk - 1) / kChunk; }
+
+// Workspace regions, each 256-byte aligned, sized for n_slots = capacity.
+struct Workspace {
+  float* norms;       // [slices][n_slots]
+  float* rowmean;     // [slices][n_slots]
+  int32_t* counts;    // [slices][n_slots]
+  float* importance;  // [slices][n_slots]
+  float* stats;       // [slices][chunks][RKV_MAX_QROWS][2] (chunk max, chunk sum of exp)
+  float* ssum;        // [slices][chunks][kHeadDim] (chunk sum of unit keys)
+  int32_t* keep;      // [slices][budget]
+  size_t bytes;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline Workspace carve(const rkv_params& p, void* base) {
+  const size_t slices = (size_t)p.num_layers * p.batch * p.num_kv_heads;
+  const size_t cap = (size_t)p.capacity;
+  const size_t chunks = (size_t)chunks_of(p.capacity);
+  Workspace w;
+  size_t off = 0;
+  char* b = (char*)base;
+  auto take = [&](size_t bytes) {
+    char* ptr = b ? b + off : nullptr;
+    off += align256(bytes);
+    return ptr;
+  };
+  w.norms = (float*)take(slices * cap * 4);
+  w.rowmean = (float*)take(slices * cap * 4);
+  w.counts = (int32_t*)take(slices * cap * 4);
+  w.importance = (float*)take(slices * cap * 4);
+  w.stats = (float*)take(slices * chunks * RKV_MAX_QROWS * 2 * 4);
+  w.ssum = (float*)take(slices * chunks * kHeadDim * 4);
+  w.keep = (int32_t*)take(slices * (size_t)p.budget * 4);
+  w.bytes = off;
+  return w;
+}
+
+// Kernel launchers (one translation unit each). They return the hipError_t
+// of the launch as an int (0 = success).
+int launch_stats(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q, const int32_t* seq_start,
+                 float* norms, int32_t* counts, float* stats, float* ssum, void* stream);
+int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q, const int32_t* seq_start,
+                const float* norms, const float* stats, const float* ssum, float* importance, float* rowmean,
+                int32_t* counts, void* stream);
+int launch_redundancy(const Geom& g, const int32_t* seq_start, const int32_t* counts, const float* rowmean,
+                      float* redundancy, void* stream);
+int launch_select(const Geom& g, const float* importance, const float* redundancy, const int32_t* counts,
+                  const float* rowmean, const int32_t* seq_start, int32_t* keep, float* z_out, float* r_out,
+                  void* stream);
+int launch_compact(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const int32_t* keep,
+                   int32_t* seq_start, void* stream);
+
+}  // namespace rkv

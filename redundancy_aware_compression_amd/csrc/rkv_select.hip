@@ -1,0 +1,201 @@
+// K4 — per-head selection: redundancy softmax, score combination and an
+// exact top-k by LDS radix select.
+//
+// R-KV notes page (yoonschallenge.tistory.com/1236): opening notes (keep the
+// newest 8 tokens, keep the top-scoring rest up to the budget, drop the
+// others); summary table row "final selection criterion" (importance raises
+// the score, redundancy lowers it, lambda = 0.1; the formula itself is not
+// printed — Z = lambda*I - (1-lambda)*R is the stated reading); Q&A part 2,
+// cause 3 (redundancy softmax, combination, top-k selection).
+//
+// One work-group per (layer, sequence, KV head): R = softmax of the
+// redundancy over the candidates, Z per candidate, Z mapped to an
+// order-preserving uint32 key (+0 and -0 equal), four 8-bit radix passes over
+// LDS histograms find the k-th largest key exactly, equal keys are resolved
+// towards the later slot with a suffix count, and a block prefix sum writes
+// the kept slots in ascending order. Deterministic: no float atomics, every
+// reduction has a fixed order.
+#include "rkv_device.hpp"
+
+namespace rkv {
+
+constexpr int kSelectThreads = 512;
+
+__device__ inline uint32_t order_key(float z) {
+  uint32_t u = __float_as_uint(z);
+  if ((u & 0x7FFFFFFFu) == 0u) u = 0u;  // -0 == +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// FROM_COUNTS: redundancy = counts < beta ? 0 : rowmean (the eviction step);
+// otherwise read the given redundancy array (the standalone select call).
+template <bool FROM_COUNTS>
+__global__ __launch_bounds__(kSelectThreads) void select_kernel(Geom g, const float* __restrict__ importance,
+                                                                const float* __restrict__ redundancy,
+                                                                const int32_t* __restrict__ counts,
+                                                                const float* __restrict__ rowmean,
+                                                                const int32_t* __restrict__ seq_start,
+                                                                int32_t* __restrict__ keep, float* __restrict__ z_out,
+                                                                float* __restrict__ r_out) {
+  __shared__ uint32_t keys[RKV_MAX_CAPACITY];
+  __shared__ int hist[256];
+  __shared__ float fscr[16];
+  __shared__ int iscr[16];
+  __shared__ int sel_digit, sel_above;
+
+  const int slice = blockIdx.x;
+  int l, b, h, s0, N;
+  slice_coords(g, slice, l, b, h);
+  seq_range(g, seq_start, b, s0, N);
+  const int tid = threadIdx.x, nt = blockDim.x;
+  int32_t* krow = keep + (size_t)slice * g.budget;
+  const int B = g.budget;
+
+  if (N <= B) {  // keep every valid token, right-aligned
+    for (int j = tid; j < B; j += nt) krow[j] = j >= B - N ? j + (g.n_slots - B) : -1;
+    return;
+  }
+  const int nc = N - g.alpha, kk = B - g.alpha;
+  const size_t base = (size_t)slice * g.n_slots + s0;
+  float* fk = (float*)keys;
+
+  // ---- redundancy softmax over the candidates
+  float mx = -INFINITY;
+  for (int i = tid; i < nc; i += nt) {
+    float r;
+    if (FROM_COUNTS)
+      r = counts[base + i] < g.beta ? 0.f : rowmean[base + i];
+    else
+      r = redundancy[base + i];
+    fk[i] = r;
+    mx = fmaxf(mx, r);
+  }
+  mx = block_max(mx, fscr);
+  float sum = 0.f;
+  for (int i = tid; i < nc; i += nt) {
+    const float e = __expf(fk[i] - mx);
+    fk[i] = e;
+    sum += e;
+  }
+  sum = block_sum(sum, fscr);
+  const float inv = 1.f / sum;
+  for (int i = tid; i < nc; i += nt) {
+    const float R = fk[i] * inv;
+    const float Z = g.lambda * importance[base + i] - (1.f - g.lambda) * R;
+    keys[i] = order_key(Z);
+    if (z_out) z_out[base + i] = Z;
+    if (r_out) r_out[base + i] = R;
+  }
+  __syncthreads();
+
+  // ---- radix select: exact k-th largest key T, and how many keys equal to T to take
+  uint32_t prefix = 0;
+  int need = kk;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    for (int d = tid; d < 256; d += nt) hist[d] = 0;
+    if (tid == 0) {
+      sel_digit = 0;
+      sel_above = 0;
+    }
+    __syncthreads();
+    for (int i = tid; i < nc; i += nt) {
+      const uint32_t key = keys[i];
+      if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l owns digits 4l..4l+3; suffix sums from the top digit down
+      const int c0 = hist[4 * tid], c1 = hist[4 * tid + 1], c2 = hist[4 * tid + 2], c3 = hist[4 * tid + 3];
+      const int own = c0 + c1 + c2 + c3;
+      int incl = own;  // sum over lanes >= tid
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_down(incl, o);
+        if (tid + o < 64) incl += y;
+      }
+      const int above_lane = incl - own;  // keys in digits above 4*tid+3
+      // the digit d with above(d) < need <= above(d) + hist[d] lies in exactly one lane
+      int a3 = above_lane, a2 = a3 + c3, a1 = a2 + c2, a0 = a1 + c1;
+      int d = -1, ab = 0;
+      if (a3 < need && need <= a3 + c3) { d = 4 * tid + 3; ab = a3; }
+      else if (a2 < need && need <= a2 + c2) { d = 4 * tid + 2; ab = a2; }
+      else if (a1 < need && need <= a1 + c1) { d = 4 * tid + 1; ab = a1; }
+      else if (a0 < need && need <= a0 + c0) { d = 4 * tid; ab = a0; }
+      if (d >= 0) {
+        sel_digit = d;
+        sel_above = ab;
+      }
+    }
+    __syncthreads();
+    need -= sel_above;
+    prefix |= (uint32_t)sel_digit << shift;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+
+  // ---- keys equal to T: keep the `need` latest ones. Each thread owns a
+  // contiguous range of candidates; a suffix count over threads gives every
+  // equal key the number of equal keys after it.
+  const int seg = (N + nt - 1) / nt;
+  const int lo = tid * seg, hi = min(N, lo + seg);
+  int eq_here = 0;
+  for (int i = lo; i < hi && i < nc; ++i) eq_here += keys[i] == T;
+  int eq_total;
+  const int eq_before = block_exclusive_scan(eq_here, iscr, &eq_total);
+  int eq_after = eq_total - eq_before - eq_here;  // equal keys in later threads' ranges
+
+  // ---- flags and their prefix sum give the output position of each kept slot
+  int kept_here = 0;
+  {
+    int ea = eq_after;
+    for (int i = hi - 1; i >= lo; --i) {
+      bool sel;
+      if (i >= nc) {
+        sel = true;  // observation window
+      } else {
+        const uint32_t key = keys[i];
+        sel = key > T || (key == T && ea < need);
+        if (key == T) ++ea;
+      }
+      kept_here += sel;
+    }
+  }
+  int kept_total;
+  int out = block_exclusive_scan(kept_here, iscr, &kept_total);
+  {
+    int ea = eq_after;
+    // walk backwards to reuse the suffix count, writing positions from the end of the range
+    int pos = out + kept_here;
+    for (int i = hi - 1; i >= lo; --i) {
+      bool sel;
+      if (i >= nc) {
+        sel = true;
+      } else {
+        const uint32_t key = keys[i];
+        sel = key > T || (key == T && ea < need);
+        if (key == T) ++ea;
+      }
+      if (sel && --pos < B) krow[pos] = s0 + i;  // pos < B always; the guard only bounds the write
+    }
+  }
+}
+
+int launch_select(const Geom& g, const float* importance, const float* redundancy, const int32_t* counts,
+                  const float* rowmean, const int32_t* seq_start, int32_t* keep, float* z_out, float* r_out,
+                  void* stream) {
+  const int slices = g.L * g.batch * g.H;
+  if (slices == 0) return 0;
+  hipStream_t s = (hipStream_t)stream;
+  if (counts)
+    hipLaunchKernelGGL(select_kernel<true>, dim3(slices), dim3(kSelectThreads), 0, s, g, importance, redundancy,
+                       counts, rowmean, seq_start, keep, z_out, r_out);
+  else
+    hipLaunchKernelGGL(select_kernel<false>, dim3(slices), dim3(kSelectThreads), 0, s, g, importance, redundancy,
+                       counts, rowmean, seq_start, keep, z_out, r_out);
+  return (int)hipGetLastError();
+}
+
+}  // namespace rkv

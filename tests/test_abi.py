@@ -1,0 +1,164 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/rkv.h declares, and rejects bad arguments on the host before any
+launch (so no call here touches device memory)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import redundancy_aware_compression_amd as rkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rkv.h")
+
+# Fake device pointers: never dereferenced, because every call below fails
+# validation or takes a documented no-launch path.
+FAKE = 0x10000
+FAKE_WS = 0x100000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rkv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["rkv_workspace_bytes", "rkv_score", "rkv_select", "rkv_compact", "rkv_evict_step",
+              "rkv_status_string", "rkv_last_hip_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(rkv.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), f"librkv.so does not export {name}"
+
+
+def P(**kw):
+    base = dict(num_layers=2, batch=2, num_kv_heads=2, group=4, capacity=384, budget=256)
+    base.update(kw)
+    return rkv.make_params(**base)
+
+
+def layers(n=2, ptr=FAKE):
+    return [ptr + 4096 * i for i in range(n)]
+
+
+def test_status_strings():
+    for code, name in rkv.STATUS.items():
+        assert rkv.rkv_status_string(code) == name
+    assert rkv.rkv_last_hip_error() == 0
+
+
+def test_workspace_bytes():
+    p = P()
+    n = rkv.rkv_workspace_bytes(p)
+    slices = 2 * 2 * 2
+    assert n >= slices * 384 * 4 * 4 + slices * 256 * 4
+    assert n % 256 == 0
+    assert rkv.rkv_workspace_bytes(P(budget=8, obs_window=8)) == 0
+    assert rkv.rkv_workspace_bytes(P(capacity=100)) == 0
+
+
+BAD_PARAMS = [
+    (dict(lam=1.5), "RKV_ERR_BAD_PARAM"),
+    (dict(lam=-0.1), "RKV_ERR_BAD_PARAM"),
+    (dict(lam=float("nan")), "RKV_ERR_BAD_PARAM"),
+    (dict(tau=1.5), "RKV_ERR_BAD_PARAM"),
+    (dict(beta=-1), "RKV_ERR_BAD_PARAM"),
+    (dict(dtype=7), "RKV_ERR_BAD_PARAM"),
+    (dict(num_layers=0), "RKV_ERR_BAD_SHAPE"),
+    (dict(num_layers=129), "RKV_ERR_BAD_SHAPE"),
+    (dict(batch=0), "RKV_ERR_BAD_SHAPE"),
+    (dict(num_kv_heads=0), "RKV_ERR_BAD_SHAPE"),
+    (dict(group=0), "RKV_ERR_BAD_SHAPE"),
+    (dict(obs_window=0), "RKV_ERR_BAD_SHAPE"),
+    (dict(budget=8), "RKV_ERR_BAD_SHAPE"),  # budget must exceed the window
+    (dict(buffer=0), "RKV_ERR_BAD_SHAPE"),
+    (dict(capacity=383), "RKV_ERR_BAD_SHAPE"),  # < budget + buffer
+    (dict(head_dim=64), "RKV_ERR_UNSUPPORTED"),
+    (dict(capacity=20000), "RKV_ERR_UNSUPPORTED"),
+    (dict(group=9), "RKV_ERR_UNSUPPORTED"),  # 9 * 8 query rows > 64
+]
+
+
+@pytest.mark.parametrize("kw,expect", BAD_PARAMS, ids=[str(b[0]) for b in BAD_PARAMS])
+def test_bad_params_rejected_by_every_entry_point(kw, expect):
+    p = P(**kw)
+    code = [k for k, v in rkv.STATUS.items() if v == expect][0]
+    assert rkv.rkv_score(p, layers(), FAKE, FAKE, 300, FAKE, FAKE, None, FAKE_WS, 1 << 40, stream=0,
+                         check=False) == code
+    assert rkv.rkv_select(p, FAKE, FAKE, FAKE, 300, FAKE, stream=0, check=False) == code
+    assert rkv.rkv_compact(p, layers(), layers(), FAKE, FAKE, 300, stream=0, check=False) == code
+    st, ns = rkv.rkv_evict_step(p, layers(), layers(), FAKE, FAKE, 384, FAKE_WS, 1 << 40, stream=0, check=False)
+    assert st == code and ns == 384
+
+
+def st_of(name):
+    return [k for k, v in rkv.STATUS.items() if v == name][0]
+
+
+def test_null_and_alignment_errors():
+    p = P()
+    big = 1 << 40
+    NULL, MIS = st_of("RKV_ERR_NULL_ARG"), st_of("RKV_ERR_MISALIGNED")
+    assert rkv.rkv_score(p, [FAKE, 0], FAKE, FAKE, 300, FAKE, FAKE, None, FAKE_WS, big, stream=0, check=False) == NULL
+    assert rkv.rkv_score(p, layers(), 0, FAKE, 300, FAKE, FAKE, None, FAKE_WS, big, stream=0, check=False) == NULL
+    assert rkv.rkv_score(p, layers(), FAKE, 0, 300, FAKE, FAKE, None, FAKE_WS, big, stream=0, check=False) == NULL
+    assert rkv.rkv_score(p, layers(), FAKE, FAKE, 300, 0, FAKE, None, FAKE_WS, big, stream=0, check=False) == NULL
+    assert rkv.rkv_score(p, layers(), FAKE, FAKE, 300, FAKE, FAKE, None, 0, big, stream=0, check=False) == NULL
+    assert rkv.rkv_score(p, [FAKE + 8, FAKE], FAKE, FAKE, 300, FAKE, FAKE, None, FAKE_WS, big, stream=0,
+                         check=False) == MIS
+    assert rkv.rkv_score(p, layers(), FAKE + 4, FAKE, 300, FAKE, FAKE, None, FAKE_WS, big, stream=0,
+                         check=False) == MIS
+    assert rkv.rkv_score(p, layers(), FAKE, FAKE, 300, FAKE, FAKE, None, FAKE_WS + 16, big, stream=0,
+                         check=False) == MIS
+    assert rkv.rkv_select(p, 0, FAKE, FAKE, 300, FAKE, stream=0, check=False) == NULL
+    assert rkv.rkv_select(p, FAKE, FAKE, FAKE, 300, 0, stream=0, check=False) == NULL
+    assert rkv.rkv_compact(p, layers(), [0, FAKE], FAKE, FAKE, 300, stream=0, check=False) == NULL
+    assert rkv.rkv_compact(p, layers(), layers(), 0, FAKE, 300, stream=0, check=False) == NULL
+    assert rkv.rkv_compact(p, layers(), [FAKE, FAKE + 2], FAKE, FAKE, 300, stream=0, check=False) == MIS
+    st, _ = rkv.rkv_evict_step(p, layers(), layers(), FAKE, 0, 384, FAKE_WS, big, stream=0, check=False)
+    assert st == NULL
+    st, _ = rkv.rkv_evict_step(p, layers(), layers(), FAKE, FAKE, 384, 0, big, stream=0, check=False)
+    assert st == NULL
+
+
+def test_slot_range_and_workspace_errors():
+    p = P()
+    SHAPE, WS = st_of("RKV_ERR_BAD_SHAPE"), st_of("RKV_ERR_WORKSPACE_TOO_SMALL")
+    need = rkv.rkv_workspace_bytes(p)
+    assert rkv.rkv_score(p, layers(), FAKE, FAKE, 385, FAKE, FAKE, None, FAKE_WS, need, stream=0,
+                         check=False) == SHAPE
+    assert rkv.rkv_score(p, layers(), FAKE, FAKE, -1, FAKE, FAKE, None, FAKE_WS, need, stream=0,
+                         check=False) == SHAPE
+    assert rkv.rkv_score(p, layers(), FAKE, FAKE, 300, FAKE, FAKE, None, FAKE_WS, need - 1, stream=0,
+                         check=False) == WS
+    assert rkv.rkv_select(p, FAKE, FAKE, FAKE, 255, FAKE, stream=0, check=False) == SHAPE  # below budget
+    assert rkv.rkv_select(p, FAKE, FAKE, FAKE, 385, FAKE, stream=0, check=False) == SHAPE
+    assert rkv.rkv_compact(p, layers(), layers(), FAKE, FAKE, 255, stream=0, check=False) == SHAPE
+    st, ns = rkv.rkv_evict_step(p, layers(), layers(), FAKE, FAKE, 385, FAKE_WS, need, stream=0, check=False)
+    assert st == SHAPE and ns == 385
+    st, ns = rkv.rkv_evict_step(p, layers(), layers(), FAKE, FAKE, 384, FAKE_WS, need - 256, stream=0, check=False)
+    assert st == WS and ns == 384
+
+
+def test_no_launch_paths_return_ok():
+    """Below the trigger the step launches nothing; scoring with n_slots <= budget
+    has nothing to score. Both succeed without touching the fake pointers."""
+    p = P()
+    need = rkv.rkv_workspace_bytes(p)
+    for ns in (0, 1, 255, 256, 383):
+        st, out = rkv.rkv_evict_step(p, layers(), layers(), FAKE, FAKE, ns, FAKE_WS, need, stream=0, check=False)
+        assert st == 0 and out == ns
+    for ns in (0, 100, 256):
+        assert rkv.rkv_score(p, layers(), FAKE, FAKE, ns, FAKE, FAKE, None, FAKE_WS, need, stream=0,
+                             check=False) == 0
+
+
+def test_python_raises_on_error():
+    with pytest.raises(rkv.RkvError, match="RKV_ERR_BAD_PARAM"):
+        rkv.rkv_select(P(lam=2.0), FAKE, FAKE, FAKE, 300, FAKE, stream=0)

@@ -1,0 +1,254 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the same
+seeded inputs. Small workloads compare every slice; the full-size workloads
+compare a fixed sample of slices the oracle can afford, plus properties that
+hold at any size (self-consistent top-k, bit-exact compaction of every slice).
+"""
+import numpy as np
+import pytest
+
+import _gpu
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    # ragged lengths (some sequences below the budget), several 128-key tiles, ragged tail
+    "small_ragged": synth.small("small_ragged", 101, num_layers=2, batch=3, num_kv_heads=2, group=4, budget=256,
+                                lengths=("uniform", 200, 384)),
+    # group 5 (40 query rows: two MFMA row tiles), n_slots 400 is not a multiple of 64
+    "small_g5": synth.small("small_g5", 102, num_layers=1, batch=1, num_kv_heads=3, group=5, budget=300, buffer=100),
+    # window 4, group 3, capacity past n_slots (canary rows)
+    "small_a4": synth.small("small_a4", 103, num_layers=1, batch=2, num_kv_heads=2, group=3, budget=200, buffer=77,
+                            obs_window=4, extra_capacity=40),
+    # stronger repetition so that many tokens lose protection
+    "small_dup": synth.small("small_dup", 104, num_layers=1, batch=1, num_kv_heads=4, group=4, budget=256,
+                             copy_frac=0.6, span_len=16),
+    "single_f32": synth.WORKLOADS["single_f32"],
+}
+
+# (workload, sampled (layer, sequence, head) slices)
+FULL = {
+    "llama8b_b1": [(0, 0, 0), (0, 0, 7), (7, 0, 5), (15, 0, 3), (31, 0, 0), (31, 0, 7)],
+    "llama8b_b32_ragged": None,  # sampled from the evicting sequences below
+    "qwen14b_b8": [(0, 0, 0), (47, 7, 7)],
+}
+
+_cache = {}
+
+
+def cache_of(name):
+    """Host inputs of a workload (seed 0) and a fresh device copy."""
+    if name not in _cache:
+        w = SMALL.get(name) or synth.WORKLOADS[name]
+        _cache.clear()  # keep at most one workload resident
+        _cache[name] = synth.build_cache(w, seed=0)
+    cs = _cache[name]
+    return cs, _gpu.DevCache.of(cs)
+
+
+def sample_of(name, cs):
+    w = cs.w
+    if name in SMALL:
+        return [(l, b, h) for l in range(w.num_layers) for b in range(w.batch) for h in range(w.num_kv_heads)]
+    if FULL[name] is not None:
+        return FULL[name]
+    ev = [b for b in range(w.batch) if cs.lengths[b] > w.budget]
+    non = [b for b in range(w.batch) if cs.lengths[b] <= w.budget]
+    picks = [(0, ev[0], 0), (31, ev[-1], 7), (16, ev[len(ev) // 2], 3), (5, ev[1 % len(ev)], 2), (0, non[0], 0)]
+    return picks
+
+
+ALL = list(SMALL) + list(FULL)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_score_parity(name):
+    cs, dc = cache_of(name)
+    w = cs.w
+    imp, red, cnt = _gpu.gpu_score(dc)
+    band_rows = 0
+    for (l, b, h) in sample_of(name, cs):
+        s = _gpu.slice_index(w, l, b, h)
+        s0, N = int(cs.seq_start[b]), int(cs.lengths[b])
+        ref = _gpu.oracle_slice(cs, l, b, h)
+        if N <= w.budget:
+            assert np.all(cnt[s] == -7), "non-evicting sequences must not be scored"
+            continue
+        band_rows += _gpu.check_scores(ref, imp[s, s0:], red[s, s0:], cnt[s, s0:], what=f"{name} {(l, b, h)}")
+    print(f"{name}: rows with a pair in the tau band: {band_rows}")
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_select_parity(name):
+    """Selection fed with the oracle's own scores (as fp32)."""
+    cs, dc = cache_of(name)
+    w = cs.w
+    n = cs.n_slots
+    sample = sample_of(name, cs)
+    imp = np.zeros((w.slices, n), np.float32)
+    red = np.zeros((w.slices, n), np.float32)
+    refs = {}
+    for (l, b, h) in sample:
+        s = _gpu.slice_index(w, l, b, h)
+        s0, N = int(cs.seq_start[b]), int(cs.lengths[b])
+        ref = _gpu.oracle_slice(cs, l, b, h)
+        refs[(l, b, h)] = ref
+        if N > w.budget:
+            imp[s, s0:] = ref.importance
+            red[s, s0:] = ref.rbar
+    keep, z, r = _gpu.gpu_select(dc, imp, red)
+    ndiff = 0
+    for (l, b, h), ref in refs.items():
+        s = _gpu.slice_index(w, l, b, h)
+        s0, N = int(cs.seq_start[b]), int(cs.lengths[b])
+        row = keep[s]
+        assert np.all(row[: w.budget - min(N, w.budget)] == -1)
+        rel = _gpu.keep_rel_of(row, s0)
+        if N > w.budget:
+            nc = N - w.obs_window
+            eps = _gpu.REL_TOL * (w.lam * ref.importance[:nc] + (1 - w.lam) * ref.R[:nc])
+            assert np.all(np.abs(z[s, s0:s0 + nc] - ref.Z[:nc]) <= eps + 1e-12), f"{name} Z"
+            assert np.all(np.abs(r[s, s0:s0 + nc] - ref.R[:nc]) <= _gpu.REL_TOL * ref.R[:nc]), f"{name} R"
+            _gpu.check_self_topk(rel, z[s, s0:], w, N, what=f"{name} {(l, b, h)}")
+        ndiff += _gpu.check_keep(rel, ref, w, N, what=f"{name} {(l, b, h)}")
+    print(f"{name}: kept-set differences inside the band: {ndiff}")
+
+
+def _random_keep(rng, B, n_slots, N):
+    """A valid keep row: ascending sources, right-aligned, keep[j] >= j."""
+    kept = min(N, B)
+    s0 = n_slots - N
+    if N <= B:
+        src = s0 + np.arange(N)
+    else:
+        mode = rng.integers(0, 4)
+        if mode == 0:  # drop a random subset
+            src = s0 + np.sort(rng.choice(N, size=B, replace=False))
+        elif mode == 1:  # drop only the oldest (every row moves by the same offset)
+            src = s0 + np.arange(N - B, N)
+        elif mode == 2:  # drop only the newest candidates (long stable prefix)
+            src = s0 + np.concatenate([np.arange(B - 8), np.arange(N - 8, N)])
+        else:  # drop one early token (every later row shifts by one)
+            src = s0 + np.delete(np.arange(N), 3)[:B]
+    row = np.full(B, -1, np.int32)
+    row[B - kept:] = src
+    return row
+
+
+@pytest.mark.parametrize("name", ["small_ragged", "small_a4", "single_f32", "llama8b_b1"])
+def test_compact_bit_exact(name):
+    """In-place compaction vs a plain gather of the pre-step bytes, adversarial keep patterns."""
+    import redundancy_aware_compression_amd as rkv
+
+    torch, dev = _gpu.torch_dev()
+    cs, dc = cache_of(name)
+    w = cs.w
+    rng = np.random.default_rng(5)
+    keep = np.stack([_random_keep(rng, w.budget, cs.n_slots, int(cs.lengths[b]))
+                     for l in range(w.num_layers) for b in range(w.batch) for h in range(w.num_kv_heads)])
+    tk = torch.from_numpy(keep.reshape(-1)).to(dev)
+    rkv.rkv_compact(_gpu.params_of(w), dc.k_layers(), dc.v_layers(), tk, dc.seq_start, cs.n_slots)
+    torch.cuda.synchronize()
+    K1 = _gpu.to_host(dc.K, cs.K.dtype)
+    V1 = _gpu.to_host(dc.V, cs.V.dtype)
+    s_new = dc.seq_start.cpu().numpy()
+    for l in range(w.num_layers):
+        for b in range(w.batch):
+            for h in range(w.num_kv_heads):
+                row = keep[_gpu.slice_index(w, l, b, h)]
+                exp_k = oracle.gather_rows(cs.K[l, b, h], row)
+                exp_v = oracle.gather_rows(cs.V[l, b, h], row)
+                m = row >= 0
+                assert np.array_equal(K1[l, b, h, :w.budget][m].view(np.uint8), exp_k[m].view(np.uint8))
+                assert np.array_equal(V1[l, b, h, :w.budget][m].view(np.uint8), exp_v[m].view(np.uint8))
+                # padding destinations and rows past the budget are not written
+                assert np.array_equal(K1[l, b, h, :w.budget][~m].view(np.uint8),
+                                      cs.K[l, b, h, :w.budget][~m].view(np.uint8))
+                assert np.array_equal(K1[l, b, h, w.budget:].view(np.uint8), cs.K[l, b, h, w.budget:].view(np.uint8))
+            assert s_new[b] == w.budget - min(int(cs.lengths[b]), w.budget)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_evict_step(name):
+    """The whole step: its compaction equals the gather of the pre-step bytes
+    by the keep set that score + select produce (bit-exact, every slice), and
+    that keep set matches the oracle's under the band rule (sampled slices)."""
+    import redundancy_aware_compression_amd as rkv
+
+    torch, dev = _gpu.torch_dev()
+    cs, dc = cache_of(name)
+    w = cs.w
+    imp, red, _ = _gpu.gpu_score(dc)
+    keep, z, _ = _gpu.gpu_select(dc, imp, red)
+    p = _gpu.params_of(w)
+    wsb = rkv.rkv_workspace_bytes(p)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    st, ns = rkv.rkv_evict_step(p, dc.k_layers(), dc.v_layers(), dc.Q, dc.seq_start, cs.n_slots, ws, wsb)
+    torch.cuda.synchronize()
+    assert ns == w.budget
+    s_new = dc.seq_start.cpu().numpy()
+    K1 = _gpu.to_host(dc.K, cs.K.dtype)
+    V1 = _gpu.to_host(dc.V, cs.V.dtype)
+    del dc
+    for l in range(w.num_layers):
+        for b in range(w.batch):
+            kept = min(int(cs.lengths[b]), w.budget)
+            assert s_new[b] == w.budget - kept
+            for h in range(w.num_kv_heads):
+                row = keep[_gpu.slice_index(w, l, b, h)]
+                src = row[w.budget - kept:]
+                assert np.all(src >= 0) and np.all(row[: w.budget - kept] == -1)
+                assert np.array_equal(K1[l, b, h, w.budget - kept:w.budget], cs.K[l, b, h][src])
+                assert np.array_equal(V1[l, b, h, w.budget - kept:w.budget], cs.V[l, b, h][src])
+                if w.capacity > w.n_slots:
+                    assert np.array_equal(K1[l, b, h, w.n_slots:].view(np.uint8),
+                                          cs.K[l, b, h, w.n_slots:].view(np.uint8))
+    ndiff = 0
+    for (l, b, h) in sample_of(name, cs):
+        s = _gpu.slice_index(w, l, b, h)
+        s0, N = int(cs.seq_start[b]), int(cs.lengths[b])
+        ref = _gpu.oracle_slice(cs, l, b, h)
+        rel = _gpu.keep_rel_of(keep[s], s0)
+        if N > w.budget:
+            _gpu.check_self_topk(rel, z[s, s0:], w, N, what=f"{name} {(l, b, h)}")
+        ndiff += _gpu.check_keep(rel, ref, w, N, what=f"{name} {(l, b, h)}")
+    print(f"{name}: kept-set differences inside the band: {ndiff}")
+
+
+def test_noop_below_trigger():
+    """Below budget + buffer nothing is launched and the cache is bit-identical."""
+    import redundancy_aware_compression_amd as rkv
+
+    torch, dev = _gpu.torch_dev()
+    cs, dc = cache_of("small_ragged")
+    w = cs.w
+    p = _gpu.params_of(w)
+    wsb = rkv.rkv_workspace_bytes(p)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    st, ns = rkv.rkv_evict_step(p, dc.k_layers(), dc.v_layers(), dc.Q, dc.seq_start, w.n_slots - 1, ws, wsb)
+    torch.cuda.synchronize()
+    assert ns == w.n_slots - 1
+    assert np.array_equal(_gpu.to_host(dc.K, cs.K.dtype).view(np.uint8), cs.K.view(np.uint8))
+    assert np.array_equal(dc.seq_start.cpu().numpy(), cs.seq_start)
+
+
+def test_deterministic():
+    """Two steps on identical inputs give bit-identical caches and scores."""
+    import redundancy_aware_compression_amd as rkv
+
+    torch, dev = _gpu.torch_dev()
+    cs, _ = cache_of("small_dup")
+    w = cs.w
+    outs = []
+    for _ in range(2):
+        dc = _gpu.DevCache.of(cs)
+        imp, red, cnt = _gpu.gpu_score(dc)
+        p = _gpu.params_of(w)
+        wsb = rkv.rkv_workspace_bytes(p)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        rkv.rkv_evict_step(p, dc.k_layers(), dc.v_layers(), dc.Q, dc.seq_start, cs.n_slots, ws, wsb)
+        torch.cuda.synchronize()
+        outs.append((imp, red, cnt, _gpu.to_host(dc.K, cs.K.dtype), _gpu.to_host(dc.V, cs.V.dtype)))
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
