@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the R-KV decode-time eviction step on one MI355X.
+
+One step = one rkv_evict_step over every (layer, sequence, KV head) slice of
+the workload: statistics, Gram/importance, selection and in-place
+compaction, i.e. the whole hot path. Default workload: the Llama-8B-shaped
+GQA cache (32 layers, 8 KV heads, group 4, head_dim 128, batch 1, budget
+1024 + buffer 128, window 8, beta 2, lambda 0.1, tau 0.5), seeded synthetic
+keys with ~30 % repeated spans.
+
+Timing: W warm-up steps, then K timed steps between two device
+synchronisations. Before every step the pristine pre-eviction cache is
+restored by a device-to-device copy and (default) a 512 MiB buffer is
+written to evict the 256 MiB last-level cache, so the step reads its inputs
+from HBM; both happen outside the step's HIP-event window. The step and each
+of its four kernels are timed with HIP events recorded on the launch stream
+(rkv_evict_step_timed). value = 1000 / mean step milliseconds.
+
+Prints ONE JSON line. `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "R-KV eviction steps/s (all layers×KV heads), µs/step; %MFMA & %HBM peak"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (timing plumbing only)."""
+
+    def __init__(self):
+        # by soname, so that the runtime torch (and librkv) already use is reused
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        with open("/proc/self/maps") as f:
+            copies = {line.split()[-1] for line in f if "libamdhip64" in line}
+        assert len(copies) == 1, f"more than one HIP runtime mapped: {copies}"
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            ev = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+            out.append(ev.value)
+        return out
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return float(ms.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def percentile(xs, q):
+    s = sorted(xs)
+    i = min(len(s) - 1, max(0, int(round(q / 100.0 * (len(s) - 1)))))
+    return s[i]
+
+
+def cpu_baseline(cs, budget_s: float = 20.0):
+    """The CPU oracle (single-threaded per slice, as written) over a bounded
+    sample of the workload's slices, one slice per task on a thread pool."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    w = cs.w
+    cores = min(16, os.cpu_count() or 1)
+    slices = [(l, b, h) for l in range(w.num_layers) for b in range(w.batch) for h in range(w.num_kv_heads)]
+    evicting = [s for s in slices if cs.lengths[s[1]] > w.budget]
+    # estimate one slice's cost, then size the sample to ~budget_s of CPU work
+
+    def run(sl):
+        l, b, h = sl
+        s0 = int(cs.seq_start[b])
+        r = oracle.slice_eval(cs.K[l, b, h, s0:cs.n_slots], cs.Q[l, b, h * w.group:(h + 1) * w.group],
+                              budget=w.budget, obs_window=w.obs_window, beta=w.beta, lam=w.lam, tau=w.tau)
+        src = np.full(w.budget, -1, np.int32)
+        src[w.budget - r.kept:] = s0 + r.keep
+        oracle.gather_rows(cs.K[l, b, h], src)
+        oracle.gather_rows(cs.V[l, b, h], src)
+        return r.kept
+
+    t = time.perf_counter()
+    run(evicting[0])
+    one = time.perf_counter() - t
+    n = max(1, min(len(evicting), int(budget_s / max(one, 1e-6))))
+    rng = np.random.default_rng(0)
+    sample = [evicting[i] for i in sorted(rng.choice(len(evicting), size=n, replace=False))]
+    t = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        list(ex.map(run, sample))
+    wall = time.perf_counter() - t
+    step_s = wall * len(evicting) / n  # non-evicting slices only shift rows; not counted
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {len(evicting)} evicting slices (score, select, K/V gather), one slice per task "
+                      f"on {cores} threads; step time extrapolated from the sample's wall time",
+            "ms_per_step": step_s * 1e3, "cpu_seconds": one * n}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b_b1")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-flush", action="store_true", help="keep inputs warm in the last-level cache")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the eviction step has no cross-GPU exchange and this build runs on a "
+              "single MI355X; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import redundancy_aware_compression_amd as rkv
+
+    w = synth.WORKLOADS[args.workload]
+    cs = synth.build_cache(w, seed=args.seed)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    hip = HipEvents()
+
+    def dev_tensor(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    with torch.cuda.stream(stream):
+        K0, V0, Q = dev_tensor(cs.K), dev_tensor(cs.V), dev_tensor(cs.Q)
+        S0 = torch.from_numpy(cs.seq_start.copy()).to(dev)
+        K, V, S = K0.clone(), V0.clone(), S0.clone()
+        p = rkv.make_params(w.num_layers, w.batch, w.num_kv_heads, w.group, w.capacity, w.budget, w.buffer,
+                            w.obs_window, w.beta, w.lam, w.tau, w.dtype)
+        wsb = rkv.rkv_workspace_bytes(p)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        k_layers = [K[l] for l in range(w.num_layers)]
+        v_layers = [V[l] for l in range(w.num_layers)]
+
+        # moved rows (keep[j] != j) of this input, for the compaction's algorithmic bytes
+        n = cs.n_slots
+        imp = torch.zeros(w.slices * n, dtype=torch.float32, device=dev)
+        red = torch.zeros_like(imp)
+        keep = torch.empty(w.slices * w.budget, dtype=torch.int32, device=dev)
+        rkv.rkv_score(p, k_layers, Q, S, n, imp, red, None, ws, wsb, stream=stream)
+        rkv.rkv_select(p, imp, red, S, n, keep, stream=stream)
+        stream.synchronize()
+        kp = keep.cpu().numpy().reshape(w.slices, w.budget)
+        moved = int(((kp >= 0) & (kp != np.arange(w.budget)[None, :])).sum())
+        del imp, red, keep
+
+        def one_step(evs):
+            K.copy_(K0)
+            V.copy_(V0)
+            S.copy_(S0)
+            if not args.no_flush:
+                flush.zero_()
+            st, ns = rkv.rkv_evict_step_timed(p, k_layers, v_layers, Q, S, n, ws, wsb, evs, stream=stream)
+            assert ns == w.budget
+
+        warm = hip.create(5)
+        for _ in range(args.warmup):
+            one_step(warm)
+        evs = [hip.create(5) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            one_step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+
+    step_ms = [hip.elapsed_ms(e[0], e[4]) for e in evs]
+    stage_ms = [[hip.elapsed_ms(e[s], e[s + 1]) for e in evs] for s in range(4)]
+    for e in evs + [warm]:
+        hip.destroy(e)
+    mean_ms = sum(step_ms) / len(step_ms)
+
+    # algorithmic work per launch (evicting slices only)
+    e = w.elem_bytes
+    D, G, A = w.head_dim, w.group, w.obs_window
+    ev_lens = [int(cs.lengths[b]) for b in range(w.batch) if cs.lengths[b] > w.budget]
+    per_seq_slices = w.num_layers * w.num_kv_heads
+    k1_bytes = per_seq_slices * sum(N * D * e + G * A * D * e + 8 * N for N in ev_lens)
+    k3_flops = per_seq_slices * sum(D * N * (N - 1) + 2 * G * A * N * D for N in ev_lens)
+    k4_bytes = per_seq_slices * sum(12 * N for N in ev_lens) + w.slices * w.budget * 4
+    k5_bytes = 4 * D * e * moved
+    names = ["stats", "gram", "select", "compact"]
+    means = [sum(x) / len(x) for x in stage_ms]
+    mfma_peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    kernels = {
+        "stats": {"us": means[0] * 1e3, "bound": "hbm", "bytes": k1_bytes,
+                  "achieved": k1_bytes / (means[0] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"},
+        "gram": {"us": means[1] * 1e3, "bound": "mfma", "flops": k3_flops,
+                 "achieved": k3_flops / (means[1] * 1e-3) / 1e12, "peak": mfma_peak, "unit": "TFLOP/s"},
+        "select": {"us": means[2] * 1e3, "bound": "latency", "bytes": k4_bytes,
+                   "achieved": k4_bytes / (means[2] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"},
+        "compact": {"us": means[3] * 1e3, "bound": "hbm", "bytes": k5_bytes, "moved_rows": moved,
+                    "achieved": k5_bytes / (means[3] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"},
+    }
+    for k in kernels.values():
+        k["frac"] = k["achieved"] / k["peak"]
+    dom = max(["stats", "gram", "compact"], key=lambda k: kernels[k]["us"])
+    dk = kernels[dom]
+    roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
+                "unit": dk["unit"], "frac": dk["frac"], "traffic": None}
+
+    out = {
+        "metric": METRIC,
+        "value": 1000.0 / mean_ms,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": mean_ms,
+        "us_per_step": mean_ms * 1e3,
+        "us_p10": percentile(step_ms, 10) * 1e3,
+        "us_p90": percentile(step_ms, 90) * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.num_layers, "batch": w.batch, "kv_heads": w.num_kv_heads,
+                   "group": w.group, "head_dim": w.head_dim, "budget": w.budget, "buffer": w.buffer,
+                   "obs_window": w.obs_window, "beta": w.beta, "lambda": w.lam, "tau": w.tau,
+                   "slices": w.slices, "n_slots": cs.n_slots, "llc_flush": not args.no_flush, "seed": args.seed},
+        "wall_ms_per_iteration": wall * 1e3 / args.steps,
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cs)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

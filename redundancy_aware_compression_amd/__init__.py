@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     make_params,
     rkv_compact,
     rkv_evict_step,
+    rkv_evict_step_timed,
     rkv_last_hip_error,
     rkv_score,
     rkv_select,

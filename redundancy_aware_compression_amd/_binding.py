@@ -86,6 +86,8 @@ def _lib():
         L.rkv_compact.argtypes = [P, vp, vp, vp, vp, i32, vp]
         L.rkv_evict_step.restype = ctypes.c_int
         L.rkv_evict_step.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(i32), vp, sz, vp]
+        L.rkv_evict_step_timed.restype = ctypes.c_int
+        L.rkv_evict_step_timed.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(i32), vp, sz, vp, vp]
         L.rkv_status_string.restype = ctypes.c_char_p
         L.rkv_status_string.argtypes = [ctypes.c_int]
         L.rkv_last_hip_error.restype = ctypes.c_int
@@ -166,4 +168,18 @@ def rkv_evict_step(p: RkvParams, k_layers: Sequence, v_layers: Sequence, obs_q, 
                                ctypes.byref(ns), _ptr(ws), ws_bytes, _stream(stream))
     if check:
         _check(st, "rkv_evict_step")
+    return st, ns.value
+
+
+def rkv_evict_step_timed(p: RkvParams, k_layers: Sequence, v_layers: Sequence, obs_q, seq_start, n_slots: int, ws,
+                         ws_bytes: int, stage_events: Sequence[int], stream=None, check: bool = True):
+    """rkv_evict_step recording 5 caller-created hipEvent_t handles between its stages."""
+    ns = ctypes.c_int32(n_slots)
+    ev = (ctypes.c_void_p * 5)(*stage_events)
+    st = _lib().rkv_evict_step_timed(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
+                                     ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(obs_q),
+                                     _ptr(seq_start), ctypes.byref(ns), _ptr(ws), ws_bytes, _stream(stream),
+                                     ctypes.cast(ev, ctypes.c_void_p))
+    if check:
+        _check(st, "rkv_evict_step_timed")
     return st, ns.value

@@ -1,6 +1,7 @@
 // librkv C ABI: argument validation, workspace carving and kernel sequencing.
 // Validation runs entirely on the host before anything is enqueued, so every
 // error path leaves device memory untouched and needs no GPU.
+#include <hip/hip_runtime_api.h>
 #include <string.h>
 
 #include "rkv.h"
@@ -119,8 +120,9 @@ rkv_status rkv_score(const rkv_params* p, const void* const* k_layers, const voi
   const rkv::LayerPtrs kl = make_layers(p, k_layers);
   int32_t* cnt = counts ? counts : w.counts;
   RKV_TRY(rkv::launch_stats(g, p->dtype, kl, obs_q, seq_start, w.norms, cnt, w.stats, w.ssum, stream));
-  RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, w.norms, w.stats, w.ssum, importance, w.rowmean, cnt,
-                           stream));
+  RKV_TRY(rkv::launch_reduce_stats(g, seq_start, w.stats, w.ssum, w.rowstat, w.svec, stream));
+  RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, w.norms, w.rowstat, w.svec, importance, w.rowmean,
+                           cnt, stream));
   RKV_TRY(rkv::launch_redundancy(g, seq_start, cnt, w.rowmean, redundancy, stream));
   return RKV_OK;
 }
@@ -151,8 +153,9 @@ rkv_status rkv_compact(const rkv_params* p, void* const* k_layers, void* const* 
   return RKV_OK;
 }
 
-rkv_status rkv_evict_step(const rkv_params* p, void* const* k_layers, void* const* v_layers, const void* obs_q,
-                          int32_t* seq_start, int32_t* n_slots, void* ws, size_t ws_bytes, void* stream) {
+rkv_status rkv_evict_step_timed(const rkv_params* p, void* const* k_layers, void* const* v_layers,
+                                const void* obs_q, int32_t* seq_start, int32_t* n_slots, void* ws, size_t ws_bytes,
+                                void* stream, void* const* stage_events) {
   rkv_status st = check_params(p);
   if (st != RKV_OK) return st;
   if ((st = check_layers(p, (const void* const*)k_layers)) != RKV_OK) return st;
@@ -168,14 +171,29 @@ rkv_status rkv_evict_step(const rkv_params* p, void* const* k_layers, void* cons
   const rkv::Geom g = make_geom(p, ns);
   const rkv::LayerPtrs kl = make_layers(p, (const void* const*)k_layers);
   const rkv::LayerPtrs vl = make_layers(p, (const void* const*)v_layers);
+  auto mark = [&](int i) -> int {
+    if (!stage_events || !stage_events[i]) return 0;
+    return (int)hipEventRecord((hipEvent_t)stage_events[i], (hipStream_t)stream);
+  };
+  RKV_TRY(mark(0));
   RKV_TRY(rkv::launch_stats(g, p->dtype, kl, obs_q, seq_start, w.norms, w.counts, w.stats, w.ssum, stream));
-  RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, w.norms, w.stats, w.ssum, w.importance, w.rowmean,
+  RKV_TRY(rkv::launch_reduce_stats(g, seq_start, w.stats, w.ssum, w.rowstat, w.svec, stream));
+  RKV_TRY(mark(1));
+  RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, w.norms, w.rowstat, w.svec, w.importance, w.rowmean,
                            w.counts, stream));
+  RKV_TRY(mark(2));
   RKV_TRY(rkv::launch_select(g, w.importance, nullptr, w.counts, w.rowmean, seq_start, w.keep, nullptr, nullptr,
                              stream));
+  RKV_TRY(mark(3));
   RKV_TRY(rkv::launch_compact(g, p->dtype, kl, vl, w.keep, seq_start, stream));
+  RKV_TRY(mark(4));
   *n_slots = p->budget;
   return RKV_OK;
+}
+
+rkv_status rkv_evict_step(const rkv_params* p, void* const* k_layers, void* const* v_layers, const void* obs_q,
+                          int32_t* seq_start, int32_t* n_slots, void* ws, size_t ws_bytes, void* stream) {
+  return rkv_evict_step_timed(p, k_layers, v_layers, obs_q, seq_start, n_slots, ws, ws_bytes, stream, nullptr);
 }
 
 }  // extern "C"

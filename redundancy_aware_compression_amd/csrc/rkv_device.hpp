@@ -85,6 +85,38 @@ __device__ inline void mma_frag(f32x16& acc, const Frag<float>& a, const Frag<fl
   }
 }
 
+// Raw buffer resources: base address, byte extent and the gfx9 descriptor
+// word 3 for 32-bit raw access. Accesses past the extent are range-checked
+// per dword by the hardware: loads return 0 (also into LDS) without touching
+// memory, so ragged tails need no clamping or branches.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
+}
+
+__device__ inline uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// 16 bytes per lane straight into LDS: lane l writes lds + 16*l (lds uniform).
+__device__ inline void buf_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+// 4 bytes per lane straight into LDS: lane l writes lds + 4*l (lds uniform).
+__device__ inline void buf_to_lds4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
+}
+
+// One lane's half-row fragment from a buffer (zeros past the extent).
+template <typename T>
+__device__ inline void frag_load_buf(Frag<T>& f, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+#pragma unroll
+  for (int i = 0; i < Frag<T>::kU4; ++i) f.v[i] = buf_load16(r, voff + 16 * i, 0);
+}
+
 // Row of the 32x32 MFMA result held in accumulator register r of a lane in
 // half `hh` (= lane / 32); the column is lane % 32.
 __device__ inline int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }

@@ -19,7 +19,7 @@ constexpr int kHeadDim = 128;    // D
 constexpr int kChunk = 128;      // keys per stats work-group
 constexpr int kColBlock = 128;   // Gram columns (older tokens) held in registers per work-group
 constexpr int kRowBlock = 64;    // Gram rows (newer tokens) staged in LDS per iteration
-constexpr int kSegBlocks = 6;    // row blocks per Gram work unit
+constexpr int kStages = 4;       // LDS ring of row blocks in flight per Gram work-group
 constexpr int kXcds = 8;         // MI355X accelerator complex dies
 
 // Geometry and method parameters common to every kernel.
@@ -35,31 +35,11 @@ struct LayerPtrs {
 };
 
 // Gram work units of one slice with N valid tokens: column block I (kColBlock
-// older tokens) against row blocks of kRowBlock newer tokens starting at the
-// diagonal, split into segments of at most kSegBlocks row blocks.
-RKV_HD inline int gram_units(int N) {
-  int u = 0;
-  for (int i = 0; i * kColBlock < N; ++i) {
-    int nj = (N - i * kColBlock + kRowBlock - 1) / kRowBlock;
-    u += (nj + kSegBlocks - 1) / kSegBlocks;
-  }
-  return u;
-}
+// older tokens) against every row block of kRowBlock newer tokens from the
+// diagonal to the end of the slice.
+RKV_HD inline int gram_units(int N) { return (N + kColBlock - 1) / kColBlock; }
 
-RKV_HD inline bool gram_unit_of(int u, int N, int& I, int& jb_lo, int& jb_hi) {
-  for (int i = 0; i * kColBlock < N; ++i) {
-    int nj = (N - i * kColBlock + kRowBlock - 1) / kRowBlock;
-    int nseg = (nj + kSegBlocks - 1) / kSegBlocks;
-    if (u < nseg) {
-      I = i;
-      jb_lo = u * kSegBlocks;
-      jb_hi = jb_lo + kSegBlocks < nj ? jb_lo + kSegBlocks : nj;
-      return true;
-    }
-    u -= nseg;
-  }
-  return false;
-}
+RKV_HD inline int gram_row_blocks(int N, int I) { return (N - I * kColBlock + kRowBlock - 1) / kRowBlock; }
 
 RKV_HD inline int chunks_of(int n) { return (n + kChunk - 1) / kChunk; }
 
@@ -71,6 +51,8 @@ struct Workspace {
   float* importance;  // [slices][n_slots]
   float* stats;       // [slices][chunks][RKV_MAX_QROWS][2] (chunk max, chunk sum of exp)
   float* ssum;        // [slices][chunks][kHeadDim] (chunk sum of unit keys)
+  float* rowstat;     // [slices][RKV_MAX_QROWS][2] (row max, 1 / row sum of exp)
+  float* svec;        // [slices][kHeadDim] (sum of unit keys)
   int32_t* keep;      // [slices][budget]
   size_t bytes;
 };
@@ -95,6 +77,8 @@ inline Workspace carve(const rkv_params& p, void* base) {
   w.importance = (float*)take(slices * cap * 4);
   w.stats = (float*)take(slices * chunks * RKV_MAX_QROWS * 2 * 4);
   w.ssum = (float*)take(slices * chunks * kHeadDim * 4);
+  w.rowstat = (float*)take(slices * RKV_MAX_QROWS * 2 * 4);
+  w.svec = (float*)take(slices * kHeadDim * 4);
   w.keep = (int32_t*)take(slices * (size_t)p.budget * 4);
   w.bytes = off;
   return w;
@@ -104,8 +88,10 @@ inline Workspace carve(const rkv_params& p, void* base) {
 // of the launch as an int (0 = success).
 int launch_stats(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q, const int32_t* seq_start,
                  float* norms, int32_t* counts, float* stats, float* ssum, void* stream);
+int launch_reduce_stats(const Geom& g, const int32_t* seq_start, const float* stats, const float* ssum,
+                        float* rowstat, float* svec, void* stream);
 int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q, const int32_t* seq_start,
-                const float* norms, const float* stats, const float* ssum, float* importance, float* rowmean,
+                const float* norms, const float* rowstat, const float* svec, float* importance, float* rowmean,
                 int32_t* counts, void* stream);
 int launch_redundancy(const Geom& g, const int32_t* seq_start, const int32_t* counts, const float* rowmean,
                       float* redundancy, void* stream);
