@@ -10,9 +10,11 @@ keys with ~30 % repeated spans.
 
 Timing: W warm-up steps, then K timed steps between two device
 synchronisations. Before every step the pristine pre-eviction cache is
-restored by a device-to-device copy and (default) a 512 MiB buffer is
-written to evict the 256 MiB last-level cache, so the step reads its inputs
-from HBM; both happen outside the step's HIP-event window. The step and each
+restored by a device-to-device copy and (default) a 512 MiB buffer is read
+to evict the 256 MiB last-level cache (reading, not writing, so that the
+evicted lines are clean and the step's reads do not pay for write-backs), so
+the step reads its inputs from HBM; both happen outside the step's HIP-event
+window. The step and each
 of its four kernels are timed with HIP events recorded on the launch stream
 (rkv_evict_step_timed). value = 1000 / mean step milliseconds.
 
@@ -157,7 +159,11 @@ def main():
                             w.obs_window, w.beta, w.lam, w.tau, w.dtype)
         wsb = rkv.rkv_workspace_bytes(p)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        # last-level-cache flush by READING 512 MiB: it leaves clean lines, so
+        # the step's own reads are not slowed by write-backs of dirty data (a
+        # write-based flush halves the read bandwidth of the following kernel)
+        flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        flush_out = torch.zeros((), dtype=torch.int64, device=dev)
         k_layers = [K[l] for l in range(w.num_layers)]
         v_layers = [V[l] for l in range(w.num_layers)]
 
@@ -178,7 +184,7 @@ def main():
             V.copy_(V0)
             S.copy_(S0)
             if not args.no_flush:
-                flush.zero_()
+                torch.sum(flush.view(torch.int64), dim=(0,), out=flush_out)
             st, ns = rkv.rkv_evict_step_timed(p, k_layers, v_layers, Q, S, n, ws, wsb, evs, stream=stream)
             assert ns == w.budget
 

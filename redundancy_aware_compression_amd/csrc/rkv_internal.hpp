@@ -17,9 +17,10 @@ namespace rkv {
 
 constexpr int kHeadDim = 128;    // D
 constexpr int kChunk = 128;      // keys per stats work-group
-constexpr int kColBlock = 128;   // Gram columns (older tokens) held in registers per work-group
-constexpr int kRowBlock = 64;    // Gram rows (newer tokens) staged in LDS per iteration
-constexpr int kStages = 4;       // LDS ring of row blocks in flight per Gram work-group
+constexpr int kRowBlock = 64;    // Gram rows (newer tokens) per LDS stage; also the columns per wave
+constexpr int kGramWaves = 4;    // waves per Gram work-group
+constexpr int kGroupCols = kGramWaves * kRowBlock;  // columns (older tokens) per Gram work-group
+constexpr int kGramRingBytes = 65536;  // LDS ring of row blocks per Gram work-group (two groups per CU)
 constexpr int kXcds = 8;         // MI355X accelerator complex dies
 
 // Geometry and method parameters common to every kernel.
@@ -34,12 +35,14 @@ struct LayerPtrs {
   const void* p[RKV_MAX_LAYERS];
 };
 
-// Gram work units of one slice with N valid tokens: column block I (kColBlock
-// older tokens) against every row block of kRowBlock newer tokens from the
-// diagonal to the end of the slice.
-RKV_HD inline int gram_units(int N) { return (N + kColBlock - 1) / kColBlock; }
+// Gram work units of one slice with N valid tokens: column group g
+// (kGroupCols older tokens) against every row block of kRowBlock newer
+// tokens from the group's first column to the end of the slice.
+RKV_HD inline int gram_units(int N) { return (N + kGroupCols - 1) / kGroupCols; }
 
-RKV_HD inline int gram_row_blocks(int N, int I) { return (N - I * kColBlock + kRowBlock - 1) / kRowBlock; }
+RKV_HD inline int gram_row_blocks(int N, int g) {
+  return (N + kRowBlock - 1) / kRowBlock - g * (kGroupCols / kRowBlock);
+}
 
 RKV_HD inline int chunks_of(int n) { return (n + kChunk - 1) / kChunk; }
 

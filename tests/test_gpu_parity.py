@@ -24,6 +24,14 @@ SMALL = {
     # stronger repetition so that many tokens lose protection
     "small_dup": synth.small("small_dup", 104, num_layers=1, batch=1, num_kv_heads=4, group=4, budget=256,
                              copy_frac=0.6, span_len=16),
+    # window sums not aligned to the MFMA row layout (window 6, 18 query rows)
+    "small_a6": synth.small("small_a6", 105, num_layers=1, batch=2, num_kv_heads=2, group=3, budget=192, buffer=64,
+                            obs_window=6),
+    # window 16 over two query-row tiles; window 64 spans both tiles (group 1)
+    "small_a16": synth.small("small_a16", 106, num_layers=1, batch=1, num_kv_heads=2, group=4, budget=160, buffer=96,
+                             obs_window=16),
+    "small_a64": synth.small("small_a64", 107, num_layers=1, batch=1, num_kv_heads=2, group=1, budget=320, buffer=50,
+                             obs_window=64),
     "single_f32": synth.WORKLOADS["single_f32"],
 }
 
