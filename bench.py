@@ -14,9 +14,12 @@ restored by a device-to-device copy and (default) a 512 MiB buffer is read
 to evict the 256 MiB last-level cache (reading, not writing, so that the
 evicted lines are clean and the step's reads do not pay for write-backs), so
 the step reads its inputs from HBM; both happen outside the step's HIP-event
-window. The step and each
-of its four kernels are timed with HIP events recorded on the launch stream
-(rkv_evict_step_timed). value = 1000 / mean step milliseconds.
+window. Each timed step (rkv_evict_step) is bracketed by two HIP events
+recorded on the launch stream; value = 1000 / mean step milliseconds. A
+second pass of K steps (rkv_evict_step_timed) records an event between
+consecutive kernels and gives each kernel's mean duration, from which the
+roofline fractions are computed; every such mark costs the stream a few
+microseconds, so that pass is not the one the step rate comes from.
 
 Prints ONE JSON line. `cpu_baseline` times the CPU oracle on a bounded
 sample of the same workload on the host cores.
@@ -25,6 +28,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -37,6 +41,48 @@ METRIC = "R-KV eviction steps/s (all layers×KV heads), µs/step; %MFMA & %HBM p
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 FP32_MFMA_PEAK_TFLOPS = 157.3
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "redundancy_aware_compression_amd", "csrc")
+# sources (and build flags) that determine each kernel's machine code
+KERNEL_SOURCES = {
+    "stats": ["rkv_stats.hip", "rkv_device.hpp", "rkv_internal.hpp"],
+    "gram": ["rkv_gram.hip", "rkv_device.hpp", "rkv_internal.hpp"],
+    "select": ["rkv_select.hip", "rkv_device.hpp", "rkv_internal.hpp"],
+    "compact": ["rkv_compact.hip", "rkv_device.hpp", "rkv_internal.hpp"],
+}
+
+
+def kernel_source_digest(kernel: str) -> str:
+    """Short digest of the sources and build script a kernel is compiled from."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    with open(os.path.join(ROOT, "redundancy_aware_compression_amd", "build.py"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (calibrated against a copy of
+    known size), or None when there is no summary or it was taken on other
+    kernel sources."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                fields[k.strip().strip("`")] = v.strip().strip("`")
+    if fields.get("source_digest") != kernel_source_digest(kernel):
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 class HipEvents:
@@ -48,15 +94,22 @@ class HipEvents:
         with open("/proc/self/maps") as f:
             copies = {line.split()[-1] for line in f if "libamdhip64" in line}
         assert len(copies) == 1, f"more than one HIP runtime mapped: {copies}"
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    # timing-only events: no system-scope fence (cache write-back and
+    # invalidate) when an event is recorded, so the marks between the step's
+    # kernels neither stall the stream nor cool the caches; results are read
+    # after a device synchronisation
+    DISABLE_SYSTEM_FENCE = 0x20000000
 
     def create(self, n):
         out = []
         for _ in range(n):
             ev = ctypes.c_void_p()
-            assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+            assert self.hip.hipEventCreateWithFlags(ctypes.byref(ev), self.DISABLE_SYSTEM_FENCE) == 0
             out.append(ev.value)
         return out
 
@@ -64,6 +117,9 @@ class HipEvents:
         ms = ctypes.c_float()
         assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
         return float(ms.value)
+
+    def record(self, ev, stream_handle):
+        assert self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream_handle)) == 0
 
     def destroy(self, evs):
         for e in evs:
@@ -179,29 +235,52 @@ def main():
         moved = int(((kp >= 0) & (kp != np.arange(w.budget)[None, :])).sum())
         del imp, red, keep
 
-        def one_step(evs):
+        sp = stream.cuda_stream
+
+        def prepare():
+            # outside the step's events: restore the pristine cache, evict the LLC
             K.copy_(K0)
             V.copy_(V0)
             S.copy_(S0)
             if not args.no_flush:
                 torch.sum(flush.view(torch.int64), dim=(0,), out=flush_out)
-            st, ns = rkv.rkv_evict_step_timed(p, k_layers, v_layers, Q, S, n, ws, wsb, evs, stream=stream)
+
+        def plain_step(ev):
+            prepare()
+            hip.record(ev[0], sp)
+            st, ns = rkv.rkv_evict_step(p, k_layers, v_layers, Q, S, n, ws, wsb, stream=stream)
+            hip.record(ev[1], sp)
+            assert ns == w.budget
+
+        def staged_step(ev):
+            prepare()
+            st, ns = rkv.rkv_evict_step_timed(p, k_layers, v_layers, Q, S, n, ws, wsb, ev, stream=stream)
             assert ns == w.budget
 
         warm = hip.create(5)
         for _ in range(args.warmup):
-            one_step(warm)
-        evs = [hip.create(5) for _ in range(args.steps)]
+            plain_step(warm)
+            staged_step(warm)
+        # timed region: K plain steps, each between two events on the launch stream
+        evs = [hip.create(2) for _ in range(args.steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            one_step(evs[i])
+            plain_step(evs[i])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        # per-kernel pass: K more steps with an event between consecutive
+        # kernels (each mark costs the stream a few microseconds, which is why
+        # the step rate above is taken without them)
+        sevs = [hip.create(5) for _ in range(args.steps)]
+        for i in range(args.steps):
+            staged_step(sevs[i])
+        torch.cuda.synchronize()
 
-    step_ms = [hip.elapsed_ms(e[0], e[4]) for e in evs]
-    stage_ms = [[hip.elapsed_ms(e[s], e[s + 1]) for e in evs] for s in range(4)]
-    for e in evs + [warm]:
+    step_ms = [hip.elapsed_ms(e[0], e[1]) for e in evs]
+    staged_ms = [hip.elapsed_ms(e[0], e[4]) for e in sevs]
+    stage_ms = [[hip.elapsed_ms(e[s], e[s + 1]) for e in sevs] for s in range(4)]
+    for e in evs + sevs + [warm]:
         hip.destroy(e)
     mean_ms = sum(step_ms) / len(step_ms)
 
@@ -232,7 +311,7 @@ def main():
     dom = max(["stats", "gram", "compact"], key=lambda k: kernels[k]["us"])
     dk = kernels[dom]
     roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
-                "unit": dk["unit"], "frac": dk["frac"], "traffic": None}
+                "unit": dk["unit"], "frac": dk["frac"], "traffic": measured_traffic(dom, w.name)}
 
     out = {
         "metric": METRIC,
@@ -245,6 +324,7 @@ def main():
         "us_per_step": mean_ms * 1e3,
         "us_p10": percentile(step_ms, 10) * 1e3,
         "us_p90": percentile(step_ms, 90) * 1e3,
+        "us_per_step_with_kernel_marks": sum(staged_ms) / len(staged_ms) * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
