@@ -27,10 +27,9 @@ rkv_status check_params(const rkv_params* p) {
   if (p->capacity > RKV_MAX_CAPACITY) return RKV_ERR_UNSUPPORTED;
   if (p->head_dim != rkv::kHeadDim) return RKV_ERR_UNSUPPORTED;
   if ((int64_t)p->group * p->obs_window > RKV_MAX_QROWS) return RKV_ERR_UNSUPPORTED;
-  // slices index a 1-D grid (times the per-slice work units) and 2-D grids' y
+  // slices index 1-D grids (times a few work-groups per slice) and 2-D grids' y
   const int64_t slices = (int64_t)p->num_layers * p->batch * p->num_kv_heads;
   if (slices > 65535) return RKV_ERR_UNSUPPORTED;
-  if (slices * rkv::gram_units(p->capacity) > 0x7FFFFFFF) return RKV_ERR_UNSUPPORTED;
   return RKV_OK;
 }
 

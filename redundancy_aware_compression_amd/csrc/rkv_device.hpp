@@ -85,36 +85,53 @@ __device__ inline void mma_frag(f32x16& acc, const Frag<float>& a, const Frag<fl
   }
 }
 
-// Raw buffer resources: base address, byte extent and the gfx9 descriptor
-// word 3 for 32-bit raw access. Accesses past the extent are range-checked
-// per dword by the hardware: loads return 0 (also into LDS) without touching
-// memory, so ragged tails need no clamping or branches.
+// Raw buffer descriptors: base address, byte extent and the gfx9 descriptor
+// word 3 for 32-bit raw access (stride 0, no swizzle). Accesses past the
+// extent are range-checked per dword by the hardware: loads return 0 (also
+// into LDS) without touching memory, so ragged tails need no clamping.
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-constexpr int kRawBufferWord3 = 0x00020000;
+constexpr uint32_t kRawBufferWord3 = 0x00020000u;
 
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferWord3);
+__device__ inline u32x4_t make_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  u32x4_t d;
+  d.x = (uint32_t)a;
+  d.y = (uint32_t)(a >> 32) & 0xFFFFu;
+  d.z = bytes;
+  d.w = kRawBufferWord3;
+  return d;
 }
 
-__device__ inline uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
+// LDS byte address of a shared-memory pointer (uniform across the wave).
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// 16 bytes per lane straight into LDS: lane l writes lds + 16*l (lds uniform).
-__device__ inline void buf_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+// Direct buffer-to-LDS loads: lane l writes lds + 16*l (or + 4*l) with the
+// bytes at voff + soff of the buffer. Issued from inline assembly on purpose:
+// the compiler cannot tell which LDS bytes such a load writes, so for the
+// builtin it makes every later LDS read wait for all of them (vmcnt(0)),
+// which would serialise a multi-stage ring. The caller orders them with
+// explicit vmcnt waits and barriers instead; the loads count in vmcnt like
+// any vector memory load. M0 holds the LDS base; one wait state separates
+// its write from the load that reads it.
+__device__ inline void dma_to_lds16(u32x4_t desc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, %3 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(desc), "s"(soff)
+      : "memory", "m0");
 }
-// 4 bytes per lane straight into LDS: lane l writes lds + 4*l (lds uniform).
-__device__ inline void buf_to_lds4(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
-}
-
-// One lane's half-row fragment from a buffer (zeros past the extent).
-template <typename T>
-__device__ inline void frag_load_buf(Frag<T>& f, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
-#pragma unroll
-  for (int i = 0; i < Frag<T>::kU4; ++i) f.v[i] = buf_load16(r, voff + 16 * i, 0);
+__device__ inline void dma_to_lds4(u32x4_t desc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, %3 offen lds"
+      :
+      : "s"(lds), "v"(voff), "s"(desc), "s"(soff)
+      : "memory", "m0");
 }
 
 // Row of the 32x32 MFMA result held in accumulator register r of a lane in

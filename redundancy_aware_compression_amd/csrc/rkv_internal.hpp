@@ -17,10 +17,9 @@ namespace rkv {
 
 constexpr int kHeadDim = 128;    // D
 constexpr int kChunk = 128;      // keys per stats work-group
-constexpr int kRowBlock = 64;    // Gram rows (newer tokens) per LDS stage; also the columns per wave
-constexpr int kGramWaves = 4;    // waves per Gram work-group
-constexpr int kGroupCols = kGramWaves * kRowBlock;  // columns (older tokens) per Gram work-group
-constexpr int kGramRingBytes = 65536;  // LDS ring of row blocks per Gram work-group (two groups per CU)
+constexpr int kRowBlock = 64;    // Gram rows (newer tokens) per LDS stage; columns per wave
+constexpr int kGramWaves = 8;    // waves per Gram work-group (one slice per work-group)
+constexpr int kGroupBlocks = kGramWaves;  // 64-column blocks per column group
 constexpr int kXcds = 8;         // MI355X accelerator complex dies
 
 // Geometry and method parameters common to every kernel.
@@ -35,14 +34,12 @@ struct LayerPtrs {
   const void* p[RKV_MAX_LAYERS];
 };
 
-// Gram work units of one slice with N valid tokens: column group g
-// (kGroupCols older tokens) against every row block of kRowBlock newer
-// tokens from the group's first column to the end of the slice.
-RKV_HD inline int gram_units(int N) { return (N + kGroupCols - 1) / kGroupCols; }
-
-RKV_HD inline int gram_row_blocks(int N, int g) {
-  return (N + kRowBlock - 1) / kRowBlock - g * (kGroupCols / kRowBlock);
-}
+// Column groups of one slice with N valid tokens: group g holds the
+// kGroupBlocks 64-token blocks of older tokens from block g*kGroupBlocks on,
+// and is paired with every row block of newer tokens from its first block to
+// the end of the slice.
+RKV_HD inline int gram_groups(int N) { return (N + kGroupBlocks * kRowBlock - 1) / (kGroupBlocks * kRowBlock); }
+RKV_HD inline int gram_row_blocks(int N, int g) { return (N + kRowBlock - 1) / kRowBlock - g * kGroupBlocks; }
 
 RKV_HD inline int chunks_of(int n) { return (n + kChunk - 1) / kChunk; }
 

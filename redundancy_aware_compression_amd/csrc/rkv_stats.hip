@@ -232,9 +232,9 @@ __global__ __launch_bounds__(256) void reduce_stats_kernel(Geom g, const int32_t
     }
     S += __shfl_xor(S, 1);
     S += __shfl_xor(S, 2);
-    if (m < g.qrows && q == 0) {
-      rowstat[((size_t)slice * RKV_MAX_QROWS + m) * 2] = M;
-      rowstat[((size_t)slice * RKV_MAX_QROWS + m) * 2 + 1] = 1.f / S;
+    if (q == 0) {  // rows past the group's queries get (0, 0): their weights vanish
+      rowstat[((size_t)slice * RKV_MAX_QROWS + m) * 2] = m < g.qrows ? M : 0.f;
+      rowstat[((size_t)slice * RKV_MAX_QROWS + m) * 2 + 1] = m < g.qrows ? 1.f / S : 0.f;
     }
   }
   // 2 threads per dimension, each over every other part
