@@ -57,20 +57,21 @@ struct Stage {
   static_assert(COUNT >= 2 && COUNT <= 8, "ring depth");
 };
 
-// Waits until at most `later` row blocks of PER direct-to-LDS loads each,
-// issued by this wave after the awaited one, are still in flight.
-template <int PER>
+// Waits until this wave's loads of the awaited row block have landed: at
+// most `later` row blocks of PER direct-to-LDS loads each, plus EXTRA other
+// loads, were issued by this wave after it.
+template <int PER, int EXTRA>
 __device__ inline void wait_later_blocks(int later) {
-  static_assert(7 * PER < 64, "vmcnt has 6 bits");
+  static_assert(7 * PER + EXTRA < 64, "vmcnt has 6 bits");
   switch (later) {
-    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
-    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER)); break;
-    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * PER)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * PER)); break;
-    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * PER)); break;
-    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * PER)); break;
-    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7 * PER)); break;
+    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(EXTRA)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER + EXTRA)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER + EXTRA)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * PER + EXTRA)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * PER + EXTRA)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * PER + EXTRA)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * PER + EXTRA)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7 * PER + EXTRA)); break;
   }
 }
 
@@ -96,14 +97,13 @@ __device__ inline void frag_from_stage(Frag<T>& f, const char* st_rows, int R, i
   for (int s = 0; s < Frag<T>::kU4; ++s) f.v[s] = *(const uint4*)(row + (((hh * (S::SLOTS / 2) + s) ^ sw) * 16));
 }
 
-// Similar-pair count of one 32x32 tile: d = tau|k_i| |k_j| - G_ij is negative
-// iff S_ij > tau; its sign bit is added (no compare / carry chain).
-__device__ inline uint32_t count_tile(const f32x16& acc, float tn, const float* nj) {
-  uint32_t c = 0;
+// Similar pairs of one 32x32 tile: d = tau|k_i| |k_j| - G_ij is negative iff
+// S_ij > tau; each sign bit is shifted into a per-lane mask (one alignbit per
+// element, no compare / carry chain), whose bits are counted once per block.
+__device__ inline uint32_t sign_bits(const f32x16& acc, float tn, const float* nj, uint32_t mask) {
 #pragma unroll
-  for (int r = 0; r < 16; r += 2)
-    c += (__float_as_uint(fmaf(tn, nj[r], -acc[r])) >> 31) + (__float_as_uint(fmaf(tn, nj[r + 1], -acc[r + 1])) >> 31);
-  return c;
+  for (int r = 0; r < 16; ++r) mask = __builtin_amdgcn_alignbit(mask, __float_as_uint(fmaf(tn, nj[r], -acc[r])), 31);
+  return mask;
 }
 // The same on the diagonal tile: only pairs whose row (newer token, index
 // jl0 + acc_row within the block) lies after the column (index il).
@@ -208,12 +208,9 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   // the tile of s rows starts as zeros: only its first rows get values
   for (int o = tid * 16; o < 32 * RB; o += kGramThreads * 16) *(uint4*)(s_lds + o) = make_uint4(0, 0, 0, 0);
 
-  // ---- loaded first: the queries (all waves), the per-slice constants
-  // (wave 0, 512 bytes each); the first ring wait covers them
-  issue_rows<T>(lds_addr(q_lds),
-                make_desc((const char*)obs_q + ((size_t)(l * g.batch + b) * g.H + h) * (size_t)g.qrows * RB,
-                          (uint32_t)g.qrows * RB),
-                voff, 0u, wave);
+  // ---- loaded first: the per-slice constants (wave 0, 512 bytes each),
+  // the first row block, the queries (all waves), then the rest of the ring;
+  // the first ring wait covers them all
   if (wave == 0 && lane < 32) {
     dma_to_lds16(make_desc(rowstat + (size_t)slice * RKV_MAX_QROWS * 2, RKV_MAX_QROWS * 8), lds_addr(rst_lds),
                  (uint32_t)lane * 16, 0u);
@@ -232,7 +229,12 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
       ibi = 0;
     }
   };
-  for (int q = 0; q < total && q < S::COUNT; ++q) issue_next(q);
+  issue_next(0);
+  issue_rows<T>(lds_addr(q_lds),
+                make_desc((const char*)obs_q + ((size_t)(l * g.batch + b) * g.H + h) * (size_t)g.qrows * RB,
+                          (uint32_t)g.qrows * RB),
+                voff, 0u, wave);
+  for (int q = 1; q < total && q < S::COUNT; ++q) issue_next(q);
 
   const float scale = 1.0f / sqrtf((float)kHeadDim);
   const int alpha = g.alpha;
@@ -250,7 +252,10 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
     // from iteration 1 on (block q' - 1 + COUNT in iteration q'), so the last
     // one issued before this wait is max(COUNT - 1, q + COUNT - 2)
     const int last = min(total - 1, max(S::COUNT - 1, q + S::COUNT - 2));
-    wait_later_blocks<S::PER>(last - q);
+    if (q == 0)
+      wait_later_blocks<S::PER, S::PER_WAVE>(last);  // the queries went out after block 0
+    else
+      wait_later_blocks<S::PER, 0>(last - q);
     __syncthreads();  // every wave's share of block q is in LDS, and every
                       // wave is done with block q - 1, whose stage is free
     if (q >= 1 && q - 1 + S::COUNT < total) issue_next(q - 1 + S::COUNT);
@@ -271,6 +276,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
           tn[f] = g.tau * fabsf(nrm_i[f]);  // a zero key (norm -1) compares as G = 0
         }
       }
+      uint32_t bits[2] = {0u, 0u};  // sign bits of the block's 32 rows per column fragment
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
         Frag<T> af;
@@ -288,13 +294,15 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
         mma_frag(acc0, af, bf[0]);
         mma_frag(acc1, af, bf[1]);
         if (__builtin_expect(!diag, 1)) {
-          cnt[0] += count_tile(acc0, tn[0], nj);
-          cnt[1] += count_tile(acc1, tn[1], nj);
+          bits[0] = sign_bits(acc0, tn[0], nj, bits[0]);
+          bits[1] = sign_bits(acc1, tn[1], nj, bits[1]);
         } else {
           cnt[0] += count_tile_masked(acc0, tn[0], nj, 32 * js, col, hh);
           cnt[1] += count_tile_masked(acc1, tn[1], nj, 32 * js, 32 + col, hh);
         }
       }
+      cnt[0] += __builtin_popcount(bits[0]);
+      cnt[1] += __builtin_popcount(bits[1]);
     }
 
     if (bi + 1 < nbg) {
