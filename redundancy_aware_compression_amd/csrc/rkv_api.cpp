@@ -118,7 +118,8 @@ rkv_status rkv_score(const rkv_params* p, const void* const* k_layers, const voi
   const rkv::Geom g = make_geom(p, n_slots);
   const rkv::LayerPtrs kl = make_layers(p, k_layers);
   int32_t* cnt = counts ? counts : w.counts;
-  RKV_TRY(rkv::launch_stats(g, p->dtype, kl, obs_q, seq_start, w.norms, cnt, w.stats, w.ssum, stream));
+  RKV_TRY(rkv::launch_stats(g, p->dtype, kl, obs_q, seq_start, w.norms, w.stats, w.ssum, w.rowstat, w.svec,
+                            stream));
   RKV_TRY(rkv::launch_reduce_stats(g, seq_start, w.stats, w.ssum, w.rowstat, w.svec, stream));
   RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, w.norms, w.rowstat, w.svec, importance, w.rowmean,
                            cnt, stream));
@@ -175,7 +176,8 @@ rkv_status rkv_evict_step_timed(const rkv_params* p, void* const* k_layers, void
     return (int)hipEventRecord((hipEvent_t)stage_events[i], (hipStream_t)stream);
   };
   RKV_TRY(mark(0));
-  RKV_TRY(rkv::launch_stats(g, p->dtype, kl, obs_q, seq_start, w.norms, w.counts, w.stats, w.ssum, stream));
+  RKV_TRY(rkv::launch_stats(g, p->dtype, kl, obs_q, seq_start, w.norms, w.stats, w.ssum, w.rowstat, w.svec,
+                            stream));
   RKV_TRY(rkv::launch_reduce_stats(g, seq_start, w.stats, w.ssum, w.rowstat, w.svec, stream));
   RKV_TRY(mark(1));
   RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, w.norms, w.rowstat, w.svec, w.importance, w.rowmean,

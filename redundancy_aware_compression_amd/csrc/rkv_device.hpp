@@ -102,6 +102,12 @@ __device__ inline u32x4_t make_desc(const void* base, uint32_t bytes) {
   return d;
 }
 
+// The same extent as a resource the compiler's own buffer intrinsics take
+// (their loads and stores are tracked by the compiler's memory counters).
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRawBufferWord3);
+}
+
 // LDS byte address of a shared-memory pointer (uniform across the wave).
 __device__ inline uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;

@@ -16,7 +16,7 @@
 namespace rkv {
 
 constexpr int kHeadDim = 128;    // D
-constexpr int kChunk = 128;      // keys per stats work-group
+constexpr int kChunk = 128;      // keys per unit of the statistics partials' bound
 constexpr int kRowBlock = 64;    // Gram rows (newer tokens) per LDS stage; columns per wave
 constexpr int kGramWaves = 8;    // waves per Gram work-group (one slice per work-group)
 constexpr int kGroupBlocks = kGramWaves;  // 64-column blocks per column group
@@ -87,7 +87,7 @@ inline Workspace carve(const rkv_params& p, void* base) {
 // Kernel launchers (one translation unit each). They return the hipError_t
 // of the launch as an int (0 = success).
 int launch_stats(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q, const int32_t* seq_start,
-                 float* norms, int32_t* counts, float* stats, float* ssum, void* stream);
+                 float* norms, float* stats, float* ssum, float* rowstat, float* svec, void* stream);
 int launch_reduce_stats(const Geom& g, const int32_t* seq_start, const float* stats, const float* ssum,
                         float* rowstat, float* svec, void* stream);
 int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q, const int32_t* seq_start,
