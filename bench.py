@@ -2,8 +2,8 @@
 """Benchmark of the R-KV decode-time eviction step on one MI355X.
 
 One step = one rkv_evict_step over every (layer, sequence, KV head) slice of
-the workload: statistics, Gram/importance, selection and in-place
-compaction, i.e. the whole hot path. Default workload: the Llama-8B-shaped
+the workload: scoring (key statistics, Gram, importance and row mean in one
+kernel), selection and in-place compaction, i.e. the whole hot path. Default workload: the Llama-8B-shaped
 GQA cache (32 layers, 8 KV heads, group 4, head_dim 128, batch 1, budget
 1024 + buffer 128, window 8, beta 2, lambda 0.1, tau 0.5), seeded synthetic
 keys with ~30 % repeated spans.
@@ -45,7 +45,6 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "redundancy_aware_compression_amd", "csrc")
 # sources (and build flags) that determine each kernel's machine code
 KERNEL_SOURCES = {
-    "stats": ["rkv_stats.hip", "rkv_device.hpp", "rkv_internal.hpp"],
     "gram": ["rkv_gram.hip", "rkv_device.hpp", "rkv_internal.hpp"],
     "select": ["rkv_select.hip", "rkv_device.hpp", "rkv_internal.hpp"],
     "compact": ["rkv_compact.hip", "rkv_device.hpp", "rkv_internal.hpp"],
@@ -257,7 +256,7 @@ def main():
             st, ns = rkv.rkv_evict_step_timed(p, k_layers, v_layers, Q, S, n, ws, wsb, ev, stream=stream)
             assert ns == w.budget
 
-        warm = hip.create(5)
+        warm = hip.create(4)
         for _ in range(args.warmup):
             plain_step(warm)
             staged_step(warm)
@@ -272,14 +271,14 @@ def main():
         # per-kernel pass: K more steps with an event between consecutive
         # kernels (each mark costs the stream a few microseconds, which is why
         # the step rate above is taken without them)
-        sevs = [hip.create(5) for _ in range(args.steps)]
+        sevs = [hip.create(4) for _ in range(args.steps)]
         for i in range(args.steps):
             staged_step(sevs[i])
         torch.cuda.synchronize()
 
     step_ms = [hip.elapsed_ms(e[0], e[1]) for e in evs]
-    staged_ms = [hip.elapsed_ms(e[0], e[4]) for e in sevs]
-    stage_ms = [[hip.elapsed_ms(e[s], e[s + 1]) for e in sevs] for s in range(4)]
+    staged_ms = [hip.elapsed_ms(e[0], e[3]) for e in sevs]
+    stage_ms = [[hip.elapsed_ms(e[s], e[s + 1]) for e in sevs] for s in range(3)]
     for e in evs + sevs + [warm]:
         hip.destroy(e)
     mean_ms = sum(step_ms) / len(step_ms)
@@ -289,26 +288,23 @@ def main():
     D, G, A = w.head_dim, w.group, w.obs_window
     ev_lens = [int(cs.lengths[b]) for b in range(w.batch) if cs.lengths[b] > w.budget]
     per_seq_slices = w.num_layers * w.num_kv_heads
-    k1_bytes = per_seq_slices * sum(N * D * e + G * A * D * e + 8 * N for N in ev_lens)
     k3_flops = per_seq_slices * sum(D * N * (N - 1) + 2 * G * A * N * D for N in ev_lens)
+    k3_bytes = per_seq_slices * sum(N * D * e + G * A * D * e + 12 * N for N in ev_lens)
     k4_bytes = per_seq_slices * sum(12 * N for N in ev_lens) + w.slices * w.budget * 4
     k5_bytes = 4 * D * e * moved
-    names = ["stats", "gram", "select", "compact"]
     means = [sum(x) / len(x) for x in stage_ms]
     mfma_peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
     kernels = {
-        "stats": {"us": means[0] * 1e3, "bound": "hbm", "bytes": k1_bytes,
-                  "achieved": k1_bytes / (means[0] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"},
-        "gram": {"us": means[1] * 1e3, "bound": "mfma", "flops": k3_flops,
-                 "achieved": k3_flops / (means[1] * 1e-3) / 1e12, "peak": mfma_peak, "unit": "TFLOP/s"},
-        "select": {"us": means[2] * 1e3, "bound": "latency", "bytes": k4_bytes,
-                   "achieved": k4_bytes / (means[2] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"},
-        "compact": {"us": means[3] * 1e3, "bound": "hbm", "bytes": k5_bytes, "moved_rows": moved,
-                    "achieved": k5_bytes / (means[3] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"},
+        "gram": {"us": means[0] * 1e3, "bound": "mfma", "flops": k3_flops, "bytes": k3_bytes,
+                 "achieved": k3_flops / (means[0] * 1e-3) / 1e12, "peak": mfma_peak, "unit": "TFLOP/s"},
+        "select": {"us": means[1] * 1e3, "bound": "latency", "bytes": k4_bytes,
+                   "achieved": k4_bytes / (means[1] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"},
+        "compact": {"us": means[2] * 1e3, "bound": "hbm", "bytes": k5_bytes, "moved_rows": moved,
+                    "achieved": k5_bytes / (means[2] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"},
     }
     for k in kernels.values():
         k["frac"] = k["achieved"] / k["peak"]
-    dom = max(["stats", "gram", "compact"], key=lambda k: kernels[k]["us"])
+    dom = max(["gram", "compact"], key=lambda k: kernels[k]["us"])
     dk = kernels[dom]
     roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
                 "unit": dk["unit"], "frac": dk["frac"], "traffic": measured_traffic(dom, w.name)}

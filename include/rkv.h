@@ -164,12 +164,12 @@ rkv_status rkv_evict_step(const rkv_params* p, void* const* k_layers, void* cons
 
 /*
  * rkv_evict_step with per-stage timing events, for benchmarks and profilers.
- * stage_events: HOST array of 5 hipEvent_t created by the caller (NULL
+ * stage_events: HOST array of 4 hipEvent_t created by the caller (NULL
  * entries are skipped). Event s is recorded on `stream` right before stage s
- * is enqueued — 0 statistics (chunk pass and per-slice reduction), 1 Gram
- * and importance, 2 selection, 3 compaction —
- * and event 4 after the last one. On the no-op path no event is recorded.
- * Everything else is exactly rkv_evict_step.
+ * is enqueued — 0 scoring (key statistics, Gram, importance and row mean in
+ * one kernel), 1 selection, 2 compaction — and event 3 after the last one.
+ * On the no-op path no event is recorded. Everything else is exactly
+ * rkv_evict_step.
  */
 rkv_status rkv_evict_step_timed(const rkv_params* p, void* const* k_layers, void* const* v_layers,
                                 const void* obs_q, int32_t* seq_start, int32_t* n_slots, void* ws, size_t ws_bytes,

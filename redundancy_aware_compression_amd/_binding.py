@@ -173,9 +173,11 @@ def rkv_evict_step(p: RkvParams, k_layers: Sequence, v_layers: Sequence, obs_q, 
 
 def rkv_evict_step_timed(p: RkvParams, k_layers: Sequence, v_layers: Sequence, obs_q, seq_start, n_slots: int, ws,
                          ws_bytes: int, stage_events: Sequence[int], stream=None, check: bool = True):
-    """rkv_evict_step recording 5 caller-created hipEvent_t handles between its stages."""
+    """rkv_evict_step recording 4 caller-created hipEvent_t handles between its stages."""
     ns = ctypes.c_int32(n_slots)
-    ev = (ctypes.c_void_p * 5)(*stage_events)
+    if len(stage_events) != 4:
+        raise ValueError("rkv_evict_step_timed takes 4 events")
+    ev = (ctypes.c_void_p * 4)(*stage_events)
     st = _lib().rkv_evict_step_timed(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
                                      ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(obs_q),
                                      _ptr(seq_start), ctypes.byref(ns), _ptr(ws), ws_bytes, _stream(stream),

@@ -118,11 +118,7 @@ rkv_status rkv_score(const rkv_params* p, const void* const* k_layers, const voi
   const rkv::Geom g = make_geom(p, n_slots);
   const rkv::LayerPtrs kl = make_layers(p, k_layers);
   int32_t* cnt = counts ? counts : w.counts;
-  RKV_TRY(rkv::launch_stats(g, p->dtype, kl, obs_q, seq_start, w.norms, w.stats, w.ssum, w.rowstat, w.svec,
-                            stream));
-  RKV_TRY(rkv::launch_reduce_stats(g, seq_start, w.stats, w.ssum, w.rowstat, w.svec, stream));
-  RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, w.norms, w.rowstat, w.svec, importance, w.rowmean,
-                           cnt, stream));
+  RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, importance, w.rowmean, cnt, stream));
   RKV_TRY(rkv::launch_redundancy(g, seq_start, cnt, w.rowmean, redundancy, stream));
   return RKV_OK;
 }
@@ -176,18 +172,13 @@ rkv_status rkv_evict_step_timed(const rkv_params* p, void* const* k_layers, void
     return (int)hipEventRecord((hipEvent_t)stage_events[i], (hipStream_t)stream);
   };
   RKV_TRY(mark(0));
-  RKV_TRY(rkv::launch_stats(g, p->dtype, kl, obs_q, seq_start, w.norms, w.stats, w.ssum, w.rowstat, w.svec,
-                            stream));
-  RKV_TRY(rkv::launch_reduce_stats(g, seq_start, w.stats, w.ssum, w.rowstat, w.svec, stream));
+  RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, w.importance, w.rowmean, w.counts, stream));
   RKV_TRY(mark(1));
-  RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, w.norms, w.rowstat, w.svec, w.importance, w.rowmean,
-                           w.counts, stream));
-  RKV_TRY(mark(2));
   RKV_TRY(rkv::launch_select(g, w.importance, nullptr, w.counts, w.rowmean, seq_start, w.keep, nullptr, nullptr,
                              stream));
-  RKV_TRY(mark(3));
+  RKV_TRY(mark(2));
   RKV_TRY(rkv::launch_compact(g, p->dtype, kl, vl, w.keep, seq_start, stream));
-  RKV_TRY(mark(4));
+  RKV_TRY(mark(3));
   *n_slots = p->budget;
   return RKV_OK;
 }

@@ -1,12 +1,16 @@
-// K3 — redundancy Gram kernel with fused importance and row mean.
+// K3 — the R-KV scoring pass: key statistics, redundancy Gram, importance
+// and row mean of one slice per work-group.
 //
-// Redundancy (R-KV notes page, yoonschallenge.tistory.com/1236, summary table
-// row "redundancy computation"; Q&A part 2, cause 3: all-pairs key cosine)
-// needs, for each valid token i, the number of newer tokens j > i whose
-// cosine S_ij = k_i.k_j / (|k_i| |k_j|) exceeds tau (the protection test for
-// the beta most recent similar tokens) and the mean cosine to the other
-// tokens. The pairwise part is a dense contraction over head_dim = 128, run
-// on the 32x32x16 bf16 MFMA with exact bf16 products and fp32 accumulation.
+// R-KV notes page, yoonschallenge.tistory.com/1236: summary table rows
+// "importance computation" (attention of the observation queries, max over
+// the GQA group) and "redundancy computation" (key cosine similarity with
+// the beta most recent similar tokens protected); Q&A part 2, cause 3
+// (key normalisation, all-pairs cosine). For each valid token i the pass
+// needs the number of newer tokens j > i whose cosine
+// S_ij = k_i.k_j / (|k_i| |k_j|) exceeds tau, the mean cosine to the other
+// tokens, and the importance. The pairwise part is a dense contraction over
+// head_dim = 128, run on the 32x32x16 bf16 MFMA with exact bf16 products and
+// fp32 accumulation.
 //
 // One work-group of 8 waves per slice walks the slice's column groups in
 // turn. Column group g is the 512 older tokens of row blocks 8g .. 8g+7
@@ -21,26 +25,40 @@
 // takes its columns from the ring there (no separate column loads), so about
 // the upper triangle j >= i is computed.
 //
-// Epilogue per element: one fma, tau*|k_i|*|k_j| - G_ij, whose sign bit (the
-// norms come from the statistics pass) is added to the count of column i in
-// the lane that owns it. Rows past the slice read as zero keys with zero
-// norm and give +0, so only the diagonal block needs the j > i mask. The
-// N x N matrix never leaves registers; each column belongs to one lane,
-// which stores its count (no atomics).
+// One iteration ahead of its Gram work every block is also read by all 8
+// waves for its row norms (fp32 from the exact bf16 values, 8 lanes per
+// row). Group 0 meets every key of the slice, so while it streams the same
+// reads give the sum of unit keys s = sum_j k_j / |k_j| and each wave takes
+// one 16x16 tile (16 keys x 16 query rows) of the observation-query logits
+// on the 16x16x32 MFMA, every lane keeping the running max and sum of exp of
+// one query row (causal mask on the newest keys). At the end of group 0 these
+// merge into the softmax statistics and s that every group's epilogue uses;
+// the keys are read from HBM once.
+//
+// Epilogue per element of the Gram: one fma, tau*|k_i|*|k_j| - G_ij, whose
+// sign bit is shifted into a per-lane mask, counted once per block. Rows
+// past the slice read as zero keys with norm 0 and give +0, so only the
+// diagonal block needs the j > i mask. The N x N matrix never leaves
+// registers; each column belongs to one lane, which stores its count (no
+// atomics).
 //
 // After a group's last row block every wave computes, for its columns, the
-// importance (observation-query attention normalised by each query row's max
-// and sum of exp from the statistics pass, mean over the window, max over
-// the GQA group; the window sums are taken in registers) and the row mean of
-// S through sum_{j != i} S_ij = khat_i . s - khat_i . khat_i with s the sum
-// of unit keys, while the ring already loads the next group's rows. The
-// queries and the per-slice constants are loaded into LDS once, first.
+// importance (the logits again, normalised by each query row's max and sum
+// of exp, mean over the window, max over the GQA group; the window sums are
+// taken in registers) and the row mean of S through
+// sum_{j != i} S_ij = khat_i . s - khat_i . khat_i, while the ring already
+// loads the next group's rows.
+#include <type_traits>
+
 #include "rkv_device.hpp"
 
 namespace rkv {
 
 constexpr int kGramThreads = kGramWaves * 64;
 static_assert(RKV_MAX_QROWS <= kRowBlock, "the query rows fill one stage-sized region");
+static_assert(kRowBlock == 8 * kGramWaves, "pre-pass: 8 lanes per row, 8 rows per wave");
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // s_waitcnt immediate for vmcnt(v), other counters unconstrained (gfx9 encoding).
 __device__ constexpr int vmcnt_imm(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -50,28 +68,27 @@ struct Stage {
   static constexpr int RB = kHeadDim * Elem<T>::kBytes;      // bytes per key row
   static constexpr int SLOTS = RB / 16;                       // 16-byte slots per row
   static constexpr int BYTES = kRowBlock * RB;                // one row block
-  static constexpr int PER_WAVE = BYTES / 1024 / kGramWaves;  // 1 KB direct loads per wave per row block
-  static constexpr int PER = PER_WAVE + 1;                    // + one norm load
+  static constexpr int PER = BYTES / 1024 / kGramWaves;       // 1 KB direct loads per wave per row block
   static constexpr int COUNT = sizeof(T) == 2 ? 8 : 3;        // ring depth (LDS: ring + queries <= 160 KB)
   static_assert(kRowBlock % kGramWaves == 0 && BYTES % (1024 * kGramWaves) == 0, "row block split");
-  static_assert(COUNT >= 2 && COUNT <= 8, "ring depth");
+  static_assert(COUNT >= 3 && COUNT <= 8, "ring depth");
 };
 
 // Waits until this wave's loads of the awaited row block have landed: at
-// most `later` row blocks of PER direct-to-LDS loads each, plus EXTRA other
-// loads, were issued by this wave after it.
-template <int PER, int EXTRA>
+// most `later` row blocks of PER direct-to-LDS loads each were issued by this
+// wave after it.
+template <int PER>
 __device__ inline void wait_later_blocks(int later) {
-  static_assert(7 * PER + EXTRA < 64, "vmcnt has 6 bits");
+  static_assert(7 * PER < 64, "vmcnt has 6 bits");
   switch (later) {
-    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(EXTRA)); break;
-    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER + EXTRA)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER + EXTRA)); break;
-    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * PER + EXTRA)); break;
-    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * PER + EXTRA)); break;
-    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * PER + EXTRA)); break;
-    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * PER + EXTRA)); break;
-    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7 * PER + EXTRA)); break;
+    case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * PER)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * PER)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * PER)); break;
+    case 6: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * PER)); break;
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(7 * PER)); break;
   }
 }
 
@@ -84,10 +101,10 @@ template <typename T>
 __device__ inline void issue_rows(uint32_t st_rows, u32x4_t r, const uint32_t* voff, uint32_t soff, int wave) {
   using S = Stage<T>;
 #pragma unroll
-  for (int q = 0; q < S::PER_WAVE; ++q) dma_to_lds16(r, st_rows + (wave * S::PER_WAVE + q) * 1024, voff[q], soff);
+  for (int q = 0; q < S::PER; ++q) dma_to_lds16(r, st_rows + (wave * S::PER + q) * 1024, voff[q], soff);
 }
 
-// MFMA operand fragment of staged row R (the lane's half hh) from a swizzled stage.
+// MFMA operand fragment (32x32 layout) of staged row R, the lane's half hh.
 template <typename T>
 __device__ inline void frag_from_stage(Frag<T>& f, const char* st_rows, int R, int hh) {
   using S = Stage<T>;
@@ -95,6 +112,86 @@ __device__ inline void frag_from_stage(Frag<T>& f, const char* st_rows, int R, i
   const int sw = R & 15;
 #pragma unroll
   for (int s = 0; s < Frag<T>::kU4; ++s) f.v[s] = *(const uint4*)(row + (((hh * (S::SLOTS / 2) + s) ^ sw) * 16));
+}
+
+// 16x16 logit tiles: lane l supplies row (l % 16) of a tile and, per MFMA,
+// the 8 (bf16, 16x16x32) or 1 (fp32, 16x16x4) dims of its quarter l / 16;
+// the result holds column l % 16 and rows 4 (l / 16) + r in register r.
+template <typename T>
+struct Tile16;
+template <>
+struct Tile16<bf16_t> {
+  struct F {
+    uint4 v[4];  // dims 32 s + 8 quarter + (0..7)
+  };
+  __device__ static void load(F& f, const char* st_rows, int R, int quarter) {
+    const char* row = st_rows + R * (kHeadDim * 2);
+    const int sw = R & 15;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) f.v[s] = *(const uint4*)(row + (((4 * s + quarter) ^ sw) * 16));
+  }
+  __device__ static void mma(f32x4& acc, const F& a, const F& b) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.v[s]),
+                                                    __builtin_bit_cast(bf16x8_t, b.v[s]), acc, 0, 0, 0);
+  }
+};
+template <>
+struct Tile16<float> {
+  struct F {
+    float v[32];  // dim 4 s + quarter
+  };
+  __device__ static void load(F& f, const char* st_rows, int R, int quarter) {
+    const char* row = st_rows + R * (kHeadDim * 4);
+    const int sw = R & 15;
+#pragma unroll
+    for (int s = 0; s < 32; ++s) f.v[s] = *(const float*)(row + ((s ^ sw) * 16) + quarter * 4);
+  }
+  __device__ static void mma(f32x4& acc, const F& a, const F& b) {
+#pragma unroll
+    for (int s = 0; s < 32; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], acc, 0, 0, 0);
+  }
+};
+
+// 16 consecutive dims [16 c, +16) of staged row R as fp32 (exact widening).
+template <typename T>
+__device__ inline void row_chunk16(float* x, const char* st_rows, int R, int c) {
+  using S = Stage<T>;
+  constexpr int SPC = S::SLOTS / 8;  // 16-byte slots per 16 dims
+  const char* row = st_rows + R * S::RB;
+  const int sw = R & 15;
+#pragma unroll
+  for (int u = 0; u < SPC; ++u) {
+    const uint4 v = *(const uint4*)(row + (((c * SPC + u) ^ sw) * 16));
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (sizeof(T) == 2) {
+        x[u * 8 + 2 * e] = __uint_as_float(w[e] << 16);
+        x[u * 8 + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      } else {
+        x[u * 4 + e] = __uint_as_float(w[e]);
+      }
+    }
+  }
+}
+
+// Sum over each aligned group of 8 lanes, in every lane of the group: two
+// quad permutations, then the mirror inside the half-row (DPP, no LDS).
+__device__ inline float sum8_dpp(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  return v;
+}
+
+// Merges the softmax statistics (m2, s2) into (m1, s1).
+__device__ inline void merge_ms(float& m1, float& s1, float m2, float s2) {
+  const float m = fmaxf(m1, m2);
+  if (m == -INFINITY) return;
+  s1 = (m1 > -INFINITY ? s1 * __expf(m1 - m) : 0.f) + (m2 > -INFINITY ? s2 * __expf(m2 - m) : 0.f);
+  m1 = m;
 }
 
 // Similar pairs of one 32x32 tile: d = tau|k_i| |k_j| - G_ij is negative iff
@@ -105,7 +202,7 @@ __device__ inline uint32_t sign_bits(const f32x16& acc, float tn, const float* n
   for (int r = 0; r < 16; ++r) mask = __builtin_amdgcn_alignbit(mask, __float_as_uint(fmaf(tn, nj[r], -acc[r])), 31);
   return mask;
 }
-// The same on the diagonal tile: only pairs whose row (newer token, index
+// The count on the diagonal tile: only pairs whose row (newer token, index
 // jl0 + acc_row within the block) lies after the column (index il).
 __device__ inline uint32_t count_tile_masked(const f32x16& acc, float tn, const float* nj, int jl0, int il, int hh) {
   uint32_t c = 0;
@@ -130,6 +227,7 @@ struct SRows;
 template <>
 struct SRows<bf16_t> {
   static constexpr int RB = kHeadDim * 2;
+  static constexpr int ROWS = 3;
   __device__ static void write(char* tile, int d, float s) {
     float rest = s;
 #pragma unroll
@@ -145,34 +243,30 @@ struct SRows<bf16_t> {
 template <>
 struct SRows<float> {
   static constexpr int RB = kHeadDim * 4;
+  static constexpr int ROWS = 1;
   __device__ static void write(char* tile, int d, float s) {
     const int byte = d * 4;
     *(float*)(tile + ((byte >> 4) << 4) + (byte & 15)) = s;  // row 0: no swizzle
   }
   __device__ static float dot(const f32x16& acc) { return acc[0]; }
 };
-template <typename T>
-__device__ inline void write_s_rows(char* tile, int d, float s) {
-  SRows<T>::write(tile, d, s);
-}
 
 template <typename T>
 __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k, const void* __restrict__ obs_q,
                                                             const int32_t* __restrict__ seq_start,
-                                                            const float* __restrict__ norms,
-                                                            const float* __restrict__ rowstat,
-                                                            const float* __restrict__ svec,
                                                             float* __restrict__ importance,
                                                             float* __restrict__ rowmean, int32_t* __restrict__ counts) {
   using S = Stage<T>;
+  using TL = Tile16<T>;
   constexpr int RB = S::RB;
 
   __shared__ __align__(16) char rows_lds[S::COUNT * S::BYTES];
   __shared__ __align__(16) char q_lds[S::BYTES];               // the slice's query rows
-  __shared__ __align__(16) float nrm_lds[S::COUNT][kRowBlock];
-  __shared__ __align__(16) float rst_lds[RKV_MAX_QROWS * 2];  // per query row: max, 1 / sum of exp
-  __shared__ __align__(16) float sv_lds[kHeadDim];            // sum of unit keys
-  __shared__ __align__(16) char s_lds[32 * RB];                // s as MFMA rows (see below), swizzled
+  __shared__ __align__(16) float nrm_lds[S::COUNT][kRowBlock];  // row norms per stage (-1: zero key, 0: past the slice)
+  __shared__ __align__(16) float rst_lds[RKV_MAX_QROWS * 2];   // per query row: max, 1 / sum of exp
+  __shared__ __align__(16) float sv_lds[kHeadDim];             // sum of unit keys
+  __shared__ __align__(16) char s_lds[32 * RB];                // s as MFMA rows; scratch before that
+  static_assert(kGramWaves * (2 * 16 * 2 + kHeadDim) * 4 <= 32 * RB, "merge scratch fits the s tile");
 
   const int slice = xcd_remap(blockIdx.x, gridDim.x);
   int l, b, h, s0, N;
@@ -183,47 +277,30 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, col = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases go to scalar registers
   const size_t srow = (size_t)slice * g.n_slots;
-  const float* norms_row = norms + srow + s0;
   const int ngroups = gram_groups(N);
   const int nrb = (N + kRowBlock - 1) / kRowBlock;  // row blocks of the slice
   // every group's row blocks in one stream: group gg contributes nrb - 8 gg
   const int total = ngroups * nrb - kGroupBlocks * ngroups * (ngroups - 1) / 2;
 
-  // the slice's valid rows and norms as range-checked buffers
+  // the slice's valid rows as a range-checked buffer
   const u32x4_t rk = make_desc(row_ptr<T>(k.p[l], g, b, h, s0), (uint32_t)N * RB);
-  const u32x4_t rn = make_desc(norms_row, (uint32_t)N * 4);
-  const uint32_t ring = lds_addr(rows_lds), nring = lds_addr(&nrm_lds[0][0]);
+  const uint32_t ring = lds_addr(rows_lds);
 
   // block-invariant per-lane offsets of the row-block loads
-  uint32_t voff[S::PER_WAVE];
+  uint32_t voff[S::PER];
 #pragma unroll
-  for (int q = 0; q < S::PER_WAVE; ++q) {
-    const int flat = (wave * S::PER_WAVE + q) * 64 + lane;
+  for (int q = 0; q < S::PER; ++q) {
+    const int flat = (wave * S::PER + q) * 64 + lane;
     const int r = flat / S::SLOTS, p = flat % S::SLOTS;
     voff[q] = (uint32_t)r * RB + (uint32_t)(p ^ (r & 15)) * 16;
   }
-  constexpr int kNormsPerWave = kRowBlock / kGramWaves;
-  const uint32_t nvoff = (uint32_t)(wave * kNormsPerWave + lane) * 4;
 
-  // the tile of s rows starts as zeros: only its first rows get values
-  for (int o = tid * 16; o < 32 * RB; o += kGramThreads * 16) *(uint4*)(s_lds + o) = make_uint4(0, 0, 0, 0);
-
-  // ---- loaded first: the per-slice constants (wave 0, 512 bytes each),
-  // the first row block, the queries (all waves), then the rest of the ring;
-  // the first ring wait covers them all
-  if (wave == 0 && lane < 32) {
-    dma_to_lds16(make_desc(rowstat + (size_t)slice * RKV_MAX_QROWS * 2, RKV_MAX_QROWS * 8), lds_addr(rst_lds),
-                 (uint32_t)lane * 16, 0u);
-    dma_to_lds16(make_desc(svec + (size_t)slice * kHeadDim, kHeadDim * 4), lds_addr(sv_lds), (uint32_t)lane * 16,
-                 0u);
-  }
-  // the issue cursor walks the stream: block ibi of group ig
+  // ---- loads: the first row block, the queries (all waves), the rest of
+  // the ring; the issue cursor walks the stream (block ibi of group ig)
   int ig = 0, ibi = 0;
   auto issue_next = [&](int q) {  // stream block q (the cursor's block) into stage q % COUNT
-    const int stg = q % S::COUNT, rbase = (ig * kGroupBlocks + ibi) * kRowBlock;
-    issue_rows<T>(ring + stg * S::BYTES, rk, voff, (uint32_t)rbase * RB, wave);
-    if (lane < kNormsPerWave)
-      dma_to_lds4(rn, nring + (stg * kRowBlock + wave * kNormsPerWave) * 4, nvoff, (uint32_t)rbase * 4);
+    const int rbase = (ig * kGroupBlocks + ibi) * kRowBlock;
+    issue_rows<T>(ring + (q % S::COUNT) * S::BYTES, rk, voff, (uint32_t)rbase * RB, wave);
     if (++ibi == nrb - ig * kGroupBlocks) {
       ++ig;
       ibi = 0;
@@ -241,28 +318,110 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   const bool pow2 = (alpha & (alpha - 1)) == 0;
   const uint32_t magic = (65536u + (uint32_t)alpha - 1u) / (uint32_t)alpha;  // m / alpha = (m * magic) >> 16 for m < 64
   const int ntile = (g.qrows + 31) >> 5;
+  const int nqt16 = (g.qrows + 15) >> 4;  // 16-row query tiles of the logit tiles
   const float inv_nm1 = 1.f / (float)(N - 1);
+
+  // ---- pre-pass state: the lane's row in the block (8 lanes per row) and
+  // its 16 dims; in group 0 also its share of s and its logit tiles
+  const int pr = 8 * wave + (lane >> 3), pc = lane & 7;
+  float run[16];  // s over the lane's rows, dims 16 pc + (0..15)
+#pragma unroll
+  for (int e = 0; e < 16; ++e) run[e] = 0.f;
+  float tM[2] = {-INFINITY, -INFINITY}, tS[2] = {0.f, 0.f};  // logit tiles wave and wave + 8
+  typename TL::F qtile[2];  // their query fragments (group 0 only), from LDS after the first barrier
+  int pg = 0, pbi = 0;  // the pre-pass cursor: block pbi of group pg
+  // norms of stream block q, and with FIRST (a group-0 block) the statistics
+  auto pre = [&](int q, auto first) {
+    constexpr bool FIRST = decltype(first)::value;
+    const int stg = q % S::COUNT;
+    const char* st = rows_lds + stg * S::BYTES;
+    const int blk = pg * kGroupBlocks + pbi;  // row block of the slice
+    float x[16];
+    row_chunk16<T>(x, st, pr, pc);
+    float ss4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ss4[e & 3] = fmaf(x[e], x[e], ss4[e & 3]);
+    const float nrm = sqrtf(sum8_dpp((ss4[0] + ss4[1]) + (ss4[2] + ss4[3])));  // the row's 8 lanes
+    const int j = blk * kRowBlock + pr;  // token of the row
+    if (pc == 0) nrm_lds[stg][pr] = j < N ? (nrm > 0.f ? nrm : -1.f) : 0.f;
+    if constexpr (FIRST) {
+      const float inv = nrm > 0.f ? 1.f / nrm : 0.f;  // rows past the slice are zeros
+#pragma unroll
+      for (int e = 0; e < 16; ++e) run[e] = fmaf(x[e], inv, run[e]);
+      // logit tiles t = wave, wave + 8: keys 16 (t % 4) .. of the block,
+      // query rows 16 (t / 4) ..; lane: query row (lane & 15), keys 4 (lane >> 4) + r
+      const bool edge = blk * kRowBlock + kRowBlock > N - alpha;  // causal or past-the-slice keys inside
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int t = wave + 8 * u;
+        if (t >= 4 * nqt16) break;
+        const int kt = t & 3, qt = t >> 2;
+        typename TL::F ka;
+        TL::load(ka, st, 16 * kt + (lane & 15), lane >> 4);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        TL::mma(acc, ka, qtile[u]);
+        const uint32_t m = 16u * qt + (uint32_t)(lane & 15);
+        const int pos = N - alpha + (int)(m - ((m * magic) >> 16) * (uint32_t)alpha);  // query's token
+        float xs[4], mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          xs[r] = acc[r] * scale;
+          if (edge) {
+            const int jr = blk * kRowBlock + 16 * kt + 4 * (lane >> 4) + r;
+            xs[r] = (jr < N && jr <= pos) ? xs[r] : -INFINITY;
+          }
+          mx = fmaxf(mx, xs[r]);
+        }
+        if (mx > -INFINITY) {
+          const float Mn = fmaxf(tM[u], mx);
+          float sum = 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sum += __expf(xs[r] - Mn);
+          tS[u] = (tM[u] > -INFINITY ? tS[u] * __expf(tM[u] - Mn) : 0.f) + sum;
+          tM[u] = Mn;
+        }
+      }
+    }
+    if (++pbi == nrb - pg * kGroupBlocks) {
+      ++pg;
+      pbi = 0;
+    }
+  };
+
+  using First = std::integral_constant<bool, true>;
+  using Later = std::integral_constant<bool, false>;
+
+  // block 0 (and the queries) landed, then its norms and statistics
+  wait_later_blocks<S::PER>(min(total, S::COUNT) - 1);
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int t = wave + 8 * u;
+    if (t < 4 * nqt16) TL::load(qtile[u], q_lds, 16 * (t >> 2) + (lane & 15), lane >> 4);
+  }
+  pre(0, First{});
 
   Frag<T> bf[2];  // this group's column keys of the wave: fragment f holds columns cbase + 32 f + (0..31)
   float tn[2] = {0.f, 0.f}, nrm_i[2] = {0.f, 0.f};
   uint32_t cnt[2] = {0u, 0u};
-  int gg = 0, bi = 0;  // the block being processed: block bi of group gg
-  for (int q = 0; q < total; ++q) {
-    // blocks issued so far: the first COUNT, then one refill per iteration
-    // from iteration 1 on (block q' - 1 + COUNT in iteration q'), so the last
-    // one issued before this wait is max(COUNT - 1, q + COUNT - 2)
-    const int last = min(total - 1, max(S::COUNT - 1, q + S::COUNT - 2));
-    if (q == 0)
-      wait_later_blocks<S::PER, S::PER_WAVE>(last);  // the queries went out after block 0
-    else
-      wait_later_blocks<S::PER, 0>(last - q);
-    __syncthreads();  // every wave's share of block q is in LDS, and every
-                      // wave is done with block q - 1, whose stage is free
-    if (q >= 1 && q - 1 + S::COUNT < total) issue_next(q - 1 + S::COUNT);
-    if (q == 0 && tid < kHeadDim) write_s_rows<T>(s_lds, tid, sv_lds[tid]);  // read after the next barrier
 
+  // the start of stream iteration q: block q + 1 must have landed for its
+  // pre-pass. Blocks issued so far: the first COUNT, then one refill per
+  // iteration from iteration 1 on (block q' - 1 + COUNT in iteration q'), the
+  // last before this wait being max(COUNT - 1, q + COUNT - 2)
+  auto advance = [&](int q) {
+    if (q + 1 < total) {
+      const int last = min(total - 1, max(S::COUNT - 1, q + S::COUNT - 2));
+      wait_later_blocks<S::PER>(last - (q + 1));
+    }
+    __syncthreads();  // block q's norms are in LDS, block q + 1 has landed, and
+                      // every wave is done with block q - 1, whose stage is free
+    if (q >= 1 && q - 1 + S::COUNT < total) issue_next(q - 1 + S::COUNT);
+  };
+
+  // Gram work of stream block q = block bi of group gg
+  auto gram_block = [&](int q, int gg, int bi) {
     const int cbase = (gg * kGroupBlocks + wave) * kRowBlock;  // the wave's columns in this group
-    const int nbg = nrb - gg * kGroupBlocks;                    // row blocks of this group
     if (bi >= wave && cbase < N) {  // row blocks before the wave's own have no pair j > i
       const int stg = q % S::COUNT;
       const char* st = rows_lds + stg * S::BYTES;
@@ -305,13 +464,73 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
       cnt[1] += __builtin_popcount(bits[1]);
     }
 
-    if (bi + 1 < nbg) {
-      ++bi;
-      continue;
+  };
+
+  // end of group 0: every key of the slice went through the pre-pass
+  auto merge_stats = [&]() {
+    // Lanes 16 apart hold the same query row (other keys); lanes 8 apart
+    // the same dims (other rows).
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      merge_ms(tM[u], tS[u], __shfl_xor(tM[u], 16), __shfl_xor(tS[u], 16));
+      merge_ms(tM[u], tS[u], __shfl_xor(tM[u], 32), __shfl_xor(tS[u], 32));
     }
-    // ---- the group's last block: counts, row mean and importance of the
-    // wave's columns (the ring keeps loading the next group's rows)
-    if (q == 0) __syncthreads();  // the s rows written in this iteration
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      run[e] += __shfl_xor(run[e], 8);
+      run[e] += __shfl_xor(run[e], 16);
+      run[e] += __shfl_xor(run[e], 32);
+    }
+    float* msc = (float*)s_lds;                  // [wave][tile u][16 rows][2]
+    float* usc = msc + kGramWaves * 2 * 16 * 2;  // [wave][128 dims]
+    if (lane < 16) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        msc[((wave * 2 + u) * 16 + lane) * 2] = tM[u];
+        msc[((wave * 2 + u) * 16 + lane) * 2 + 1] = tS[u];
+      }
+    }
+    if (lane < 8) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) usc[wave * kHeadDim + 16 * lane + e] = run[e];
+    }
+    __syncthreads();
+    // query row m: tiles t = 4 (m / 16) + kt, kt = 0..3, held by wave t % 8 in slot t / 8
+    float Mf = -INFINITY, Sf = 0.f, sd = 0.f;
+    if (tid < RKV_MAX_QROWS) {
+      const int qt = tid >> 4;
+      if (qt < nqt16) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const int t = 4 * qt + kt;
+          const int base = (((t & 7) * 2 + (t >> 3)) * 16 + (tid & 15)) * 2;
+          merge_ms(Mf, Sf, msc[base], msc[base + 1]);
+        }
+      }
+    }
+    if (tid < kHeadDim) {
+#pragma unroll
+      for (int w = 0; w < kGramWaves; ++w) sd += usc[w * kHeadDim + tid];
+    }
+    __syncthreads();  // the scratch is read: the tile of s rows replaces it
+    if (tid < RKV_MAX_QROWS) {
+      // rows past the group's queries get (0, 0): their weights vanish
+      rst_lds[2 * tid] = tid < g.qrows ? Mf : 0.f;
+      rst_lds[2 * tid + 1] = tid < g.qrows ? 1.f / Sf : 0.f;
+    }
+    for (int o = SRows<T>::ROWS * RB + tid * 16; o < 32 * RB; o += kGramThreads * 16)
+      *(uint4*)(s_lds + o) = make_uint4(0, 0, 0, 0);
+    if (tid < kHeadDim) {
+      sv_lds[tid] = sd;
+      SRows<T>::write(s_lds, tid, sd);
+    }
+    __syncthreads();
+  };
+
+  // after a group's last block: counts, row mean and importance of the
+  // wave's columns (the ring keeps loading the next group's rows)
+  auto epilogue = [&](int gg) {
+    const int cbase = (gg * kGroupBlocks + wave) * kRowBlock;
     if (cbase < N) {
       // row mean of cosine through the sum of unit keys:
       // sum_{j != i} S_ij = khat_i . s - khat_i . khat_i, k_i . s being the sum
@@ -446,8 +665,29 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
       }
     }
     cnt[0] = cnt[1] = 0u;
-    ++gg;
-    bi = 0;
+  };
+
+  // group 0, with the statistics pre-pass over every key of the slice
+  for (int q = 0; q < nrb; ++q) {
+    advance(q);
+    if (q + 1 < nrb)
+      pre(q + 1, First{});
+    else if (q + 1 < total)
+      pre(q + 1, Later{});
+    gram_block(q, 0, q);
+  }
+  merge_stats();
+  epilogue(0);
+  // the later groups
+  int q = nrb;
+  for (int gg = 1; gg < ngroups; ++gg) {
+    const int nbg = nrb - gg * kGroupBlocks;  // row blocks of this group
+    for (int bi = 0; bi < nbg; ++bi, ++q) {
+      advance(q);
+      if (q + 1 < total) pre(q + 1, Later{});
+      gram_block(q, gg, bi);
+    }
+    epilogue(gg);
   }
 }
 
@@ -466,17 +706,16 @@ __global__ void redundancy_kernel(Geom g, const int32_t* __restrict__ seq_start,
 }
 
 int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q, const int32_t* seq_start,
-                const float* norms, const float* rowstat, const float* svec, float* importance, float* rowmean,
-                int32_t* counts, void* stream) {
+                float* importance, float* rowmean, int32_t* counts, void* stream) {
   const int slices = g.L * g.batch * g.H;
   if (slices == 0) return 0;
   hipStream_t s = (hipStream_t)stream;
   if (dtype == RKV_BF16)
-    hipLaunchKernelGGL(gram_kernel<bf16_t>, dim3(slices), dim3(kGramThreads), 0, s, g, k, obs_q, seq_start, norms,
-                       rowstat, svec, importance, rowmean, counts);
+    hipLaunchKernelGGL(gram_kernel<bf16_t>, dim3(slices), dim3(kGramThreads), 0, s, g, k, obs_q, seq_start,
+                       importance, rowmean, counts);
   else
-    hipLaunchKernelGGL(gram_kernel<float>, dim3(slices), dim3(kGramThreads), 0, s, g, k, obs_q, seq_start, norms,
-                       rowstat, svec, importance, rowmean, counts);
+    hipLaunchKernelGGL(gram_kernel<float>, dim3(slices), dim3(kGramThreads), 0, s, g, k, obs_q, seq_start,
+                       importance, rowmean, counts);
   return (int)hipGetLastError();
 }
 

@@ -16,7 +16,6 @@
 namespace rkv {
 
 constexpr int kHeadDim = 128;    // D
-constexpr int kChunk = 128;      // keys per unit of the statistics partials' bound
 constexpr int kRowBlock = 64;    // Gram rows (newer tokens) per LDS stage; columns per wave
 constexpr int kGramWaves = 8;    // waves per Gram work-group (one slice per work-group)
 constexpr int kGroupBlocks = kGramWaves;  // 64-column blocks per column group
@@ -41,18 +40,11 @@ struct LayerPtrs {
 RKV_HD inline int gram_groups(int N) { return (N + kGroupBlocks * kRowBlock - 1) / (kGroupBlocks * kRowBlock); }
 RKV_HD inline int gram_row_blocks(int N, int g) { return (N + kRowBlock - 1) / kRowBlock - g * kGroupBlocks; }
 
-RKV_HD inline int chunks_of(int n) { return (n + kChunk - 1) / kChunk; }
-
 // Workspace regions, each 256-byte aligned, sized for n_slots = capacity.
 struct Workspace {
-  float* norms;       // [slices][n_slots]
   float* rowmean;     // [slices][n_slots]
   int32_t* counts;    // [slices][n_slots]
   float* importance;  // [slices][n_slots]
-  float* stats;       // [slices][chunks][RKV_MAX_QROWS][2] (chunk max, chunk sum of exp)
-  float* ssum;        // [slices][chunks][kHeadDim] (chunk sum of unit keys)
-  float* rowstat;     // [slices][RKV_MAX_QROWS][2] (row max, 1 / row sum of exp)
-  float* svec;        // [slices][kHeadDim] (sum of unit keys)
   int32_t* keep;      // [slices][budget]
   size_t bytes;
 };
@@ -62,7 +54,6 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline Workspace carve(const rkv_params& p, void* base) {
   const size_t slices = (size_t)p.num_layers * p.batch * p.num_kv_heads;
   const size_t cap = (size_t)p.capacity;
-  const size_t chunks = (size_t)chunks_of(p.capacity);
   Workspace w;
   size_t off = 0;
   char* b = (char*)base;
@@ -71,14 +62,9 @@ inline Workspace carve(const rkv_params& p, void* base) {
     off += align256(bytes);
     return ptr;
   };
-  w.norms = (float*)take(slices * cap * 4);
   w.rowmean = (float*)take(slices * cap * 4);
   w.counts = (int32_t*)take(slices * cap * 4);
   w.importance = (float*)take(slices * cap * 4);
-  w.stats = (float*)take(slices * chunks * RKV_MAX_QROWS * 2 * 4);
-  w.ssum = (float*)take(slices * chunks * kHeadDim * 4);
-  w.rowstat = (float*)take(slices * RKV_MAX_QROWS * 2 * 4);
-  w.svec = (float*)take(slices * kHeadDim * 4);
   w.keep = (int32_t*)take(slices * (size_t)p.budget * 4);
   w.bytes = off;
   return w;
@@ -86,13 +72,8 @@ inline Workspace carve(const rkv_params& p, void* base) {
 
 // Kernel launchers (one translation unit each). They return the hipError_t
 // of the launch as an int (0 = success).
-int launch_stats(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q, const int32_t* seq_start,
-                 float* norms, float* stats, float* ssum, float* rowstat, float* svec, void* stream);
-int launch_reduce_stats(const Geom& g, const int32_t* seq_start, const float* stats, const float* ssum,
-                        float* rowstat, float* svec, void* stream);
 int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q, const int32_t* seq_start,
-                const float* norms, const float* rowstat, const float* svec, float* importance, float* rowmean,
-                int32_t* counts, void* stream);
+                float* importance, float* rowmean, int32_t* counts, void* stream);
 int launch_redundancy(const Geom& g, const int32_t* seq_start, const int32_t* counts, const float* rowmean,
                       float* redundancy, void* stream);
 int launch_select(const Geom& g, const float* importance, const float* redundancy, const int32_t* counts,
