@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
     const int j = blk * kRowBlock + pr;  // token of the row
     if (pc == 0) nrm_lds[stg][pr] = j < N ? (nrm > 0.f ? nrm : -1.f) : 0.f;
     if constexpr (FIRST) {
-      const float inv = nrm > 0.f ? 1.f / nrm : 0.f;  // rows past the slice are zeros
+      const float inv = nrm > 0.f ? __builtin_amdgcn_rcpf(nrm) : 0.f;  // rows past the slice are zeros
 #pragma unroll
       for (int e = 0; e < 16; ++e) run[e] = fmaf(x[e], inv, run[e]);
       // logit tiles t = wave, wave + 8: keys 16 (t % 4) .. of the block,
