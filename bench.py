@@ -173,6 +173,182 @@ def cpu_baseline(cs, budget_s: float = 20.0):
             "ms_per_step": step_s * 1e3, "cpu_seconds": one * n}
 
 
+def kernel_table(w, ev_lens, moved, means):
+    """Per-kernel algorithmic work per launch, achieved rates against the
+    MI355X peaks, and the roofline entry of the dominant kernel. ev_lens: the
+    valid lengths of the evicting sequences; moved: rows with keep[j] != j;
+    means: mean milliseconds of the scoring, selection and compaction stages."""
+    e = w.elem_bytes
+    D, G, A = w.head_dim, w.group, w.obs_window
+    per_seq_slices = w.num_layers * w.num_kv_heads
+    k3_flops = per_seq_slices * sum(D * N * (N - 1) + 2 * G * A * N * D for N in ev_lens)
+    k3_bytes = per_seq_slices * sum(N * D * e + G * A * D * e + 12 * N for N in ev_lens)
+    k4_bytes = per_seq_slices * sum(12 * N for N in ev_lens) + w.slices * w.budget * 4
+    k5_bytes = 4 * D * e * moved
+    mfma_peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
+    kernels = {
+        "gram": {"us": means[0] * 1e3, "bound": "mfma", "flops": k3_flops, "bytes": k3_bytes,
+                 "achieved": k3_flops / (means[0] * 1e-3) / 1e12, "peak": mfma_peak, "unit": "TFLOP/s"},
+        "select": {"us": means[1] * 1e3, "bound": "latency", "bytes": k4_bytes,
+                   "achieved": k4_bytes / (means[1] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"},
+        "compact": {"us": means[2] * 1e3, "bound": "hbm", "bytes": k5_bytes, "moved_rows": moved,
+                    "achieved": k5_bytes / (means[2] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"},
+    }
+    for k in kernels.values():
+        k["frac"] = k["achieved"] / k["peak"]
+    dom = max(["gram", "compact"], key=lambda k: kernels[k]["us"])
+    dk = kernels[dom]
+    roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
+                "unit": dk["unit"], "frac": dk["frac"], "traffic": measured_traffic(dom, w.name)}
+    return kernels, roofline
+
+
+SWEEP_WORKLOADS = ("llama8b_b16_sweep10pct", "llama8b_b16_sweep1024")
+SWEEP_STEADY_FROM = 10  # rounds before this one are the sweep's warm-up
+
+
+def sweep_main(args, w):
+    """The long-generation sweep: the recipe's 125 rounds, each appending 128
+    new tokens to the cache retained by the previous round and evicting back
+    to the budget. Rounds alternate between a plain step (two events: the
+    step time) and a step with a mark between kernels (per-kernel time);
+    the steady state is the median over rounds from SWEEP_STEADY_FROM on.
+    Before every step a 512 MiB read evicts the last-level cache, outside
+    the events."""
+    import numpy as np
+    import torch
+
+    import synth
+    import redundancy_aware_compression_amd as rkv
+
+    rounds = args.rounds or synth.SweepRecipe().rounds
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    hip = HipEvents()
+    cpu = None
+    with torch.cuda.stream(stream):
+        sw = synth.Sweep(w, seed=args.seed)
+        ds = synth.DeviceSweep(sw, device=dev)
+        p = rkv.make_params(w.num_layers, w.batch, w.num_kv_heads, w.group, w.capacity, w.budget, w.buffer,
+                            w.obs_window, w.beta, w.lam, w.tau, w.dtype)
+        wsb = rkv.rkv_workspace_bytes(p)
+        koff = rkv.rkv_workspace_keep_offset(p)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        keep = ws[koff:koff + w.slices * w.budget * 4].view(torch.int32).view(w.slices, w.budget)
+        ident = torch.arange(w.budget, dtype=torch.int32, device=dev)
+        flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        flush_out = torch.zeros((), dtype=torch.int64, device=dev)
+        sp = stream.cuda_stream
+        plain, staged, moved = [], [], []
+        t0 = time.perf_counter()
+        for r in range(rounds):
+            ds.next_round(r)
+            if r == 0 and not args.no_cpu_baseline:
+                cpu = sweep_cpu_baseline(ds, w)
+            torch.sum(flush.view(torch.int64), dim=(0,), out=flush_out)
+            ev = hip.create(4)
+            if r % 2 == 0:
+                hip.record(ev[0], sp)
+                st, ns = rkv.rkv_evict_step(p, ds.k_layers(), ds.v_layers(), ds.Q, ds.seq_start, ds.n_slots, ws,
+                                            wsb, stream=stream)
+                hip.record(ev[1], sp)
+            else:
+                st, ns = rkv.rkv_evict_step_timed(p, ds.k_layers(), ds.v_layers(), ds.Q, ds.seq_start, ds.n_slots,
+                                                  ws, wsb, ev, stream=stream)
+            assert ns == w.budget
+            ds.n_slots = ns
+            mv = int((keep != ident[None, :]).sum().item())  # synchronises the stream
+            if r % 2 == 0:
+                plain.append((r, hip.elapsed_ms(ev[0], ev[1])))
+            else:
+                staged.append((r, [hip.elapsed_ms(ev[i], ev[i + 1]) for i in range(3)], mv))
+            moved.append(mv)
+            hip.destroy(ev)
+            if (r + 1) % 25 == 0:
+                print(f"[sweep] round {r + 1}/{rounds}", file=sys.stderr, flush=True)
+        wall = time.perf_counter() - t0
+
+    steady = [ms for r, ms in plain if r >= SWEEP_STEADY_FROM] or [ms for _, ms in plain]
+    med = percentile(steady, 50)
+    st_rounds = [x for x in staged if x[0] >= SWEEP_STEADY_FROM] or staged
+    means = [percentile([x[1][i] for x in st_rounds], 50) for i in range(3)]
+    mv_med = int(percentile([x[2] for x in st_rounds], 50))
+    kernels, roofline = kernel_table(w, [w.budget + w.buffer] * w.batch, mv_med, means)
+    out = {
+        "metric": METRIC,
+        "value": 1000.0 / med,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": len(steady),
+        "warmup": SWEEP_STEADY_FROM,
+        "ms_per_step": med,
+        "us_per_step": med * 1e3,
+        "us_p10": percentile(steady, 10) * 1e3,
+        "us_p90": percentile(steady, 90) * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.num_layers, "batch": w.batch, "kv_heads": w.num_kv_heads,
+                   "group": w.group, "head_dim": w.head_dim, "budget": w.budget, "buffer": w.buffer,
+                   "obs_window": w.obs_window, "beta": w.beta, "lambda": w.lam, "tau": w.tau,
+                   "slices": w.slices, "n_slots": w.budget + w.buffer, "rounds": rounds,
+                   "steady_state": f"median over rounds {SWEEP_STEADY_FROM}..{rounds - 1}, plain-step rounds",
+                   "llc_flush": True, "seed": args.seed},
+        "moved_rows_per_round": {"min": min(moved), "median": int(percentile(moved, 50)), "max": max(moved)},
+        "wall_s": wall,
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
+def sweep_cpu_baseline(ds, w, budget_s: float = 20.0):
+    """The CPU oracle on a sample of round 0's pre-eviction slices (copied
+    from the device), one slice per task on a thread pool."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+
+    cores = min(16, os.cpu_count() or 1)
+    N, G = w.budget + w.buffer, w.group
+    Qh = ds.host(ds.Q)
+
+    def get(sl):
+        l, b, h = sl
+        return ds.host(ds.K[l, b, h, :N]), ds.host(ds.V[l, b, h, :N]), Qh[l, b, h * G:(h + 1) * G]
+
+    def run(x):
+        k, v, q = x
+        r = oracle.slice_eval(k, q, budget=w.budget, obs_window=w.obs_window, beta=w.beta, lam=w.lam, tau=w.tau)
+        oracle.gather_rows(k, r.keep.astype(np.int32))
+        oracle.gather_rows(v, r.keep.astype(np.int32))
+        return r.kept
+
+    t = time.perf_counter()
+    run(get((0, 0, 0)))
+    one = time.perf_counter() - t
+    n = max(1, min(w.slices, int(budget_s / max(one, 1e-6))))
+    rng = np.random.default_rng(0)
+    picks = sorted(rng.choice(w.slices, size=n, replace=False))
+    sample = [get((int(i) // (w.batch * w.num_kv_heads), (int(i) // w.num_kv_heads) % w.batch,
+                   int(i) % w.num_kv_heads)) for i in picks]
+    t = time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        list(ex.map(run, sample))
+    wall = time.perf_counter() - t
+    step_s = wall * w.slices / n
+    return {"value": 1.0 / step_s, "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of {w.slices} slices of round 0 (score, select, K/V gather), one slice per task on "
+                      f"{cores} threads; step time extrapolated from the sample's wall time",
+            "ms_per_step": step_s * 1e3, "cpu_seconds": one * n}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +358,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-flush", action="store_true", help="keep inputs warm in the last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rounds", type=int, default=0, help="sweep workloads: rounds to run (default: the recipe's)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -196,6 +373,8 @@ def main():
     import redundancy_aware_compression_amd as rkv
 
     w = synth.WORKLOADS[args.workload]
+    if w.name in SWEEP_WORKLOADS:
+        return sweep_main(args, w)
     cs = synth.build_cache(w, seed=args.seed)
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(device=dev)
@@ -283,31 +462,8 @@ def main():
         hip.destroy(e)
     mean_ms = sum(step_ms) / len(step_ms)
 
-    # algorithmic work per launch (evicting slices only)
-    e = w.elem_bytes
-    D, G, A = w.head_dim, w.group, w.obs_window
-    ev_lens = [int(cs.lengths[b]) for b in range(w.batch) if cs.lengths[b] > w.budget]
-    per_seq_slices = w.num_layers * w.num_kv_heads
-    k3_flops = per_seq_slices * sum(D * N * (N - 1) + 2 * G * A * N * D for N in ev_lens)
-    k3_bytes = per_seq_slices * sum(N * D * e + G * A * D * e + 12 * N for N in ev_lens)
-    k4_bytes = per_seq_slices * sum(12 * N for N in ev_lens) + w.slices * w.budget * 4
-    k5_bytes = 4 * D * e * moved
-    means = [sum(x) / len(x) for x in stage_ms]
-    mfma_peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
-    kernels = {
-        "gram": {"us": means[0] * 1e3, "bound": "mfma", "flops": k3_flops, "bytes": k3_bytes,
-                 "achieved": k3_flops / (means[0] * 1e-3) / 1e12, "peak": mfma_peak, "unit": "TFLOP/s"},
-        "select": {"us": means[1] * 1e3, "bound": "latency", "bytes": k4_bytes,
-                   "achieved": k4_bytes / (means[1] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"},
-        "compact": {"us": means[2] * 1e3, "bound": "hbm", "bytes": k5_bytes, "moved_rows": moved,
-                    "achieved": k5_bytes / (means[2] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"},
-    }
-    for k in kernels.values():
-        k["frac"] = k["achieved"] / k["peak"]
-    dom = max(["gram", "compact"], key=lambda k: kernels[k]["us"])
-    dk = kernels[dom]
-    roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
-                "unit": dk["unit"], "frac": dk["frac"], "traffic": measured_traffic(dom, w.name)}
+    kernels, roofline = kernel_table(w, [int(cs.lengths[b]) for b in range(w.batch) if cs.lengths[b] > w.budget],
+                                     moved, [sum(x) / len(x) for x in stage_ms])
 
     out = {
         "metric": METRIC,

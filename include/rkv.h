@@ -94,6 +94,16 @@ typedef struct {
  * clobbered. */
 size_t rkv_workspace_bytes(const rkv_params* p);
 
+/* Byte offset, inside the workspace, of the keep lists rkv_evict_step writes:
+ * int32 [num_layers][batch][num_kv_heads][budget], the same convention as
+ * rkv_select's keep (source slot of each destination slot, ascending,
+ * right-aligned, -1 before the kept entries). They stay valid after the step
+ * until the workspace is used again; a caller that keeps per-token metadata
+ * beside the cache (positions, token ids) remaps it with them (R-KV notes
+ * page, Q&A part 2, cause 3: selection indices drive the copy of the kept
+ * entries). Returns (size_t)-1 if p is invalid. */
+size_t rkv_workspace_keep_offset(const rkv_params* p);
+
 /*
  * Importance and redundancy of every valid token of every (layer, sequence,
  * KV head) whose sequence has outgrown the budget (N_b > budget); other

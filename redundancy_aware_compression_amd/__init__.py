@@ -29,4 +29,5 @@ from ._binding import (  # noqa: F401
     rkv_select,
     rkv_status_string,
     rkv_workspace_bytes,
+    rkv_workspace_keep_offset,
 )

@@ -78,6 +78,8 @@ def _lib():
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         L.rkv_workspace_bytes.restype = sz
         L.rkv_workspace_bytes.argtypes = [P]
+        L.rkv_workspace_keep_offset.restype = sz
+        L.rkv_workspace_keep_offset.argtypes = [P]
         L.rkv_score.restype = ctypes.c_int
         L.rkv_score.argtypes = [P, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
         L.rkv_select.restype = ctypes.c_int
@@ -126,6 +128,14 @@ def _check(st: int, where: str) -> int:
 
 def rkv_workspace_bytes(p: RkvParams) -> int:
     return int(_lib().rkv_workspace_bytes(ctypes.byref(p)))
+
+
+def rkv_workspace_keep_offset(p: RkvParams) -> int:
+    """Byte offset of rkv_evict_step's keep lists in the workspace; raises on invalid params."""
+    off = int(_lib().rkv_workspace_keep_offset(ctypes.byref(p)))
+    if off == ctypes.c_size_t(-1).value:
+        raise RkvError(3, "rkv_workspace_keep_offset")
+    return off
 
 
 def rkv_status_string(st: int) -> str:

@@ -87,6 +87,11 @@ size_t rkv_workspace_bytes(const rkv_params* p) {
   return rkv::carve(*p, nullptr).bytes;
 }
 
+size_t rkv_workspace_keep_offset(const rkv_params* p) {
+  if (check_params(p) != RKV_OK) return (size_t)-1;
+  return (size_t)(uintptr_t)rkv::carve(*p, (void*)(uintptr_t)256).keep - 256;
+}
+
 const char* rkv_status_string(rkv_status st) {
   switch (st) {
     case RKV_OK: return "RKV_OK";

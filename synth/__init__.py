@@ -70,8 +70,10 @@ def lib():
         L.synth_mixture_drift.argtypes = [u64, i32, i32, dbl, vp]
         L.synth_mixture_tokens.restype = None
         L.synth_mixture_tokens.argtypes = [u64, i32, i32, i32, vp, i32, vp]
-        L.synth_inject_repeats.restype = i32
-        L.synth_inject_repeats.argtypes = [u64, i32, i32, i32, dbl, dbl, vp, i32, i32, vp]
+        L.synth_repeat_plan.restype = i32
+        L.synth_repeat_plan.argtypes = [u64, i32, i32, dbl, i32, vp]
+        L.synth_repeat_apply.restype = None
+        L.synth_repeat_apply.argtypes = [u64, i32, i32, i32, vp, dbl, vp, i32, vp]
         L.synth_bf16_from_f32.restype = ctypes.c_uint16
         L.synth_bf16_from_f32.argtypes = [ctypes.c_float]
         _lib = L
@@ -288,3 +290,222 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     r = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
     r[np.isnan(f)] = BF16_NAN
     return r
+
+
+# ---------------------------------------------------------------------------
+# Long-generation sweep: 16K generated tokens as successive eviction rounds of
+# `buffer` new tokens (R-KV page, summary table, row "throughput": 16K
+# generation at a 10 % budget and at budget 1024).
+
+# stream tensor ids of round r: SWEEP_T0 + 8 (r + 1) + kind (r = -1: the
+# initial cache)
+SWEEP_T0 = 16
+K_DRIFT, K_TOKENS, K_PLAN, K_NOISE, K_VALUES, K_QUERIES = range(6)
+
+
+@dataclass(frozen=True)
+class SweepRecipe:
+    """Token recipe of the sweep: a drifting Gaussian mixture per slice
+    (same-component cosine about 0.2, below tau) with noisy repeats of
+    windows of the retained cache."""
+
+    n_comp: int = 16
+    mean_sigma: float = 0.5
+    drift_sigma: float = 0.05
+    repeat_p: float = 0.3
+    block_len: int = 32
+    noise_sigma: float = 0.05
+    rounds: int = 125
+
+
+@dataclass
+class SweepRound:
+    """Host inputs of one round before the repeats are applied."""
+
+    r: int
+    K: np.ndarray  # [L][b][H][buffer][D] new keys (mixture tokens)
+    V: np.ndarray  # [L][b][H][buffer][D] new values, N(0, 1)
+    Q: np.ndarray  # [L][b][H*G][alpha][D] observation queries, N(0, 1)
+    src: np.ndarray  # [L][b][H][buffer / block_len] window start in the retained cache, -1 = none
+
+    def window_rows(self, w: Workload) -> np.ndarray:
+        """Flat cache-row indices ((slice * capacity) + slot) of every
+        replaced block's source window, in slice-major, block order."""
+        blk = self.src.reshape(w.slices, -1)
+        sl, bi = np.nonzero(blk >= 0)
+        starts = sl.astype(np.int64) * w.capacity + blk[sl, bi]
+        bl = self.K.shape[3] // blk.shape[1]
+        return (starts[:, None] + np.arange(bl)[None, :]).reshape(-1)
+
+
+class Sweep:
+    """Seeded inputs of the long-generation sweep for a workload with
+    batch-uniform lengths: an initial cache of `budget` tokens per slice
+    (the steady state), then per round `buffer` new tokens appended after
+    them and fresh observation queries. The repeats of a round copy windows
+    of the cache retained by the previous eviction, which the caller fetches
+    (SweepRound.window_rows) from wherever that cache lives."""
+
+    def __init__(self, w: Workload, seed: int = 0, recipe: SweepRecipe = SweepRecipe(),
+                 threads: Optional[int] = None):
+        assert w.lengths == ("full",) and w.buffer % recipe.block_len == 0
+        self.w, self.seed, self.rc = w, seed, recipe
+        self.threads = threads or min(16, os.cpu_count() or 1)
+        self.tasks = [(l, b, h) for l in range(w.num_layers) for b in range(w.batch) for h in range(w.num_kv_heads)]
+        self.means = np.empty((w.slices, recipe.n_comp, w.head_dim), dtype=np.float64)
+        L = lib()
+
+        def init(i):
+            l, b, h = self.tasks[i]
+            L.synth_mixture_means(stream_key(seed, w.wid, T_MIX, l, b, h), recipe.n_comp, w.head_dim,
+                                  recipe.mean_sigma, _ptr(self.means[i]))
+
+        self._map(init)
+
+    def _map(self, fn):
+        """fn(i) for every slice i, over contiguous chunks of slices per thread."""
+        n = len(self.tasks)
+        if self.threads <= 1 or n < 4:
+            for i in range(n):
+                fn(i)
+            return
+        nch = min(n, 4 * self.threads)
+        bounds = [n * c // nch for c in range(nch + 1)]
+
+        def run(c):
+            for i in range(bounds[c], bounds[c + 1]):
+                fn(i)
+
+        with ThreadPoolExecutor(self.threads) as ex:
+            list(ex.map(run, range(nch)))
+
+    def _key(self, r, kind, l, b, h):
+        return stream_key(self.seed, self.w.wid, SWEEP_T0 + 8 * (r + 1) + kind, l, b, h)
+
+    def initial(self) -> CacheSet:
+        """Round-0 state: slots [0, budget) of every slice hold mixture tokens
+        with repeats copied from the slice's own (pre-repeat) tokens; slots
+        past the budget hold zeros; n_slots = budget."""
+        w, rc, L = self.w, self.rc, lib()
+        C, D, B = w.capacity, w.head_dim, w.budget
+        K = np.zeros((w.num_layers, w.batch, w.num_kv_heads, C, D), dtype=w.np_dtype)
+        V = np.zeros_like(K)
+        Q = np.zeros((w.num_layers, w.batch, w.q_heads, w.obs_window, D), dtype=w.np_dtype)
+        nblk = B // rc.block_len
+
+        def one(i):
+            l, b, h = self.tasks[i]
+            rows = K[l, b, h, :B]
+            L.synth_mixture_tokens(self._key(-1, K_TOKENS, l, b, h), B, D, rc.n_comp, _ptr(self.means[i]), w.code,
+                                   _ptr(rows))
+            src = np.empty(nblk, dtype=np.int32)
+            nrep = L.synth_repeat_plan(self._key(-1, K_PLAN, l, b, h), B, rc.block_len, rc.repeat_p, B, _ptr(src))
+            if nrep:
+                win = np.ascontiguousarray(
+                    np.concatenate([rows[s:s + rc.block_len] for s in src if s >= 0]))
+                L.synth_repeat_apply(self._key(-1, K_NOISE, l, b, h), B, D, rc.block_len, _ptr(src),
+                                     rc.noise_sigma, _ptr(win), w.code, _ptr(rows))
+            L.synth_fill_normal(self._key(-1, K_VALUES, l, b, h), 0.0, 1.0, w.code, _ptr(V[l, b, h, :B]), B * D)
+
+        self._map(one)
+        seq_start = np.zeros(w.batch, dtype=np.int32)
+        return CacheSet(w, self.seed, K, V, Q, seq_start, B, np.full(w.batch, B, dtype=np.int32))
+
+    def begin_round(self, r: int) -> SweepRound:
+        """Drifts the mixture and draws round r's new tokens, values, queries
+        and repeat plan (everything that does not read the retained cache)."""
+        w, rc, L = self.w, self.rc, lib()
+        n, D = w.buffer, w.head_dim
+        K = np.empty((w.num_layers, w.batch, w.num_kv_heads, n, D), dtype=w.np_dtype)
+        V = np.empty_like(K)
+        Q = np.empty((w.num_layers, w.batch, w.q_heads, w.obs_window, D), dtype=w.np_dtype)
+        src = np.empty((w.num_layers, w.batch, w.num_kv_heads, n // rc.block_len), dtype=np.int32)
+
+        def one(i):
+            l, b, h = self.tasks[i]
+            m = self.means[i]
+            L.synth_mixture_drift(self._key(r, K_DRIFT, l, b, h), rc.n_comp, D, rc.drift_sigma, _ptr(m))
+            L.synth_mixture_tokens(self._key(r, K_TOKENS, l, b, h), n, D, rc.n_comp, _ptr(m), w.code,
+                                   _ptr(K[l, b, h]))
+            L.synth_repeat_plan(self._key(r, K_PLAN, l, b, h), n, rc.block_len, rc.repeat_p, w.budget,
+                                _ptr(src[l, b, h]))
+            L.synth_fill_normal(self._key(r, K_VALUES, l, b, h), 0.0, 1.0, w.code, _ptr(V[l, b, h]), n * D)
+            qb = Q[l, b, h * w.group:(h + 1) * w.group]
+            L.synth_fill_normal(self._key(r, K_QUERIES, l, b, h), 0.0, 1.0, w.code, _ptr(qb), qb.size)
+
+        self._map(one)
+        return SweepRound(r, K, V, Q, src)
+
+    def finish_round(self, rnd: SweepRound, windows: np.ndarray) -> None:
+        """Applies the repeats: windows holds the rows of rnd.window_rows()
+        ([rows][D], storage dtype) read from the retained cache."""
+        w, rc, L = self.w, self.rc, lib()
+        D, bl = w.head_dim, rc.block_len
+        blk = rnd.src.reshape(w.slices, -1)
+        nrep = (blk >= 0).sum(axis=1)
+        first = np.concatenate([[0], np.cumsum(nrep)]) * bl
+        assert windows.shape == (int(first[-1]), D) and windows.dtype == w.np_dtype
+        Kf = rnd.K.reshape(w.slices, w.buffer, D)
+
+        def one(i):
+            if nrep[i] == 0:
+                return
+            l, b, h = self.tasks[i]
+            win = np.ascontiguousarray(windows[first[i]:first[i + 1]])
+            L.synth_repeat_apply(self._key(rnd.r, K_NOISE, l, b, h), w.buffer, D, bl, _ptr(np.ascontiguousarray(blk[i])),
+                                 rc.noise_sigma, _ptr(win), w.code, _ptr(Kf[i]))
+
+        self._map(one)
+
+
+class DeviceSweep:
+    """The sweep's cache resident on a torch device: K and V
+    [L][b][H][capacity][D] and the observation queries, as the eviction step
+    reads them. next_round(r) appends round r's tokens after the retained
+    `budget` slots (the repeats' windows are read from the device cache) and
+    leaves n_slots = budget + buffer with every sequence starting at slot 0.
+    The caller then runs the eviction step, which must bring n_slots back to
+    `budget`."""
+
+    def __init__(self, sweep: Sweep, device="cuda"):
+        import torch
+
+        self.torch, self.sweep, self.w = torch, sweep, sweep.w
+        w = self.w
+        cs = sweep.initial()
+        self.dev = torch.device(device)
+        self.K = self._up(cs.K)
+        self.V = self._up(cs.V)
+        self.Q = self._up(cs.Q)
+        del cs
+        self.seq_start = torch.zeros(w.batch, dtype=torch.int32, device=self.dev)
+        self.n_slots = w.budget
+
+    def _up(self, a: np.ndarray):
+        t = self.torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+        return t.to(self.dev)
+
+    def host(self, t) -> np.ndarray:
+        a = t.detach().cpu().numpy()
+        return a.view(np.uint16) if self.w.dtype == "bf16" else a
+
+    def k_layers(self):
+        return [self.K[l] for l in range(self.w.num_layers)]
+
+    def v_layers(self):
+        return [self.V[l] for l in range(self.w.num_layers)]
+
+    def next_round(self, r: int) -> SweepRound:
+        torch, w = self.torch, self.w
+        assert self.n_slots == w.budget, "the previous round was not evicted"
+        rnd = self.sweep.begin_round(r)
+        rows = torch.from_numpy(rnd.window_rows(w)).to(self.dev)
+        win = self.host(self.K.view(-1, w.head_dim).index_select(0, rows))
+        self.sweep.finish_round(rnd, win)
+        B, n = w.budget, w.buffer
+        self.K[:, :, :, B:B + n].copy_(torch.from_numpy(rnd.K.view(np.int16) if w.dtype == "bf16" else rnd.K))
+        self.V[:, :, :, B:B + n].copy_(torch.from_numpy(rnd.V.view(np.int16) if w.dtype == "bf16" else rnd.V))
+        self.Q.copy_(torch.from_numpy(rnd.Q.view(np.int16) if w.dtype == "bf16" else rnd.Q))
+        self.seq_start.zero_()
+        self.n_slots = B + n
+        return rnd

@@ -208,28 +208,41 @@ void synth_mixture_tokens(uint64_t key, int32_t n, int32_t d, int32_t n_comp, co
 }
 
 /*
- * Repeat injection for the long-generation sweep: the n_new rows of `fresh`
- * are taken in blocks of block_len; each block is, with probability p,
- * overwritten by a noisy (noise_sigma) copy of a uniformly placed window of
- * block_len rows of `pool` (pool_rows rows of d values, same dtype).
- * Returns the number of blocks replaced.
+ * Repeat injection for the long-generation sweep, in two steps so that the
+ * copied windows can be fetched from wherever the retained cache lives.
+ * synth_repeat_plan: the n_new new rows are taken in blocks of block_len;
+ *   for block i a uniform u and a window start src uniform in
+ *   [0, pool_rows - block_len] are drawn, and the block is replaced iff
+ *   u < p (src[i] = start) or kept (src[i] = -1). Returns the number of
+ *   replaced blocks (none when pool_rows < block_len).
+ * synth_repeat_apply: the w-th replaced block (in block order) becomes
+ *   windows[w] + N(0, noise_sigma^2) elementwise, rounded to dtype; windows
+ *   holds the replaced blocks' source rows, [replaced][block_len][d].
  */
-int32_t synth_inject_repeats(uint64_t key, int32_t n_new, int32_t d, int32_t block_len, double p,
-                             double noise_sigma, const void* pool, int32_t pool_rows, int32_t dtype,
-                             void* fresh) {
+int32_t synth_repeat_plan(uint64_t key, int32_t n_new, int32_t block_len, double p, int32_t pool_rows,
+                          int32_t* src) {
   synth_stream s = {key, 0, 0.0};
   int32_t replaced = 0;
-  if (pool_rows < block_len) return 0;
-  for (int64_t b0 = 0; b0 + block_len <= n_new; b0 += block_len) {
-    double u = unif01(&s);
-    int64_t src = unif_int(&s, (int64_t)pool_rows - block_len + 1);
-    if (u >= p) continue;
-    ++replaced;
-    for (int64_t r = 0; r < block_len; ++r)
-      for (int64_t e = 0; e < d; ++e) {
-        double v = load_val(pool, dtype, (src + r) * d + e) + noise_sigma * normal01(&s);
-        store_val(fresh, dtype, (b0 + r) * d + e, v);
-      }
+  for (int32_t i = 0; (int64_t)(i + 1) * block_len <= n_new; ++i) {
+    const double u = unif01(&s);
+    const int64_t start = pool_rows >= block_len ? unif_int(&s, (int64_t)pool_rows - block_len + 1) : 0;
+    src[i] = (pool_rows >= block_len && u < p) ? (int32_t)start : -1;
+    replaced += src[i] >= 0;
   }
   return replaced;
+}
+
+void synth_repeat_apply(uint64_t key, int32_t n_new, int32_t d, int32_t block_len, const int32_t* src,
+                        double noise_sigma, const void* windows, int32_t dtype, void* fresh) {
+  synth_stream s = {key, 0, 0.0};
+  int64_t w = 0;
+  for (int32_t i = 0; (int64_t)(i + 1) * block_len <= n_new; ++i) {
+    if (src[i] < 0) continue;
+    for (int64_t r = 0; r < block_len; ++r)
+      for (int64_t e = 0; e < d; ++e) {
+        const double v = load_val(windows, dtype, (w * block_len + r) * d + e) + noise_sigma * normal01(&s);
+        store_val(fresh, dtype, ((int64_t)i * block_len + r) * d + e, v);
+      }
+    ++w;
+  }
 }

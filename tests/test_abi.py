@@ -64,6 +64,20 @@ def test_workspace_bytes():
     assert rkv.rkv_workspace_bytes(P(capacity=100)) == 0
 
 
+def test_workspace_keep_offset():
+    """The keep lists sit inside the workspace, 256-byte aligned, with room
+    for [slices][budget] int32 entries; invalid params are rejected."""
+    for kw in [dict(), dict(budget=300, capacity=500), dict(num_layers=3, batch=5)]:
+        p = P(**kw)
+        off, n = rkv.rkv_workspace_keep_offset(p), rkv.rkv_workspace_bytes(p)
+        slices = p.num_layers * p.batch * p.num_kv_heads
+        assert off % 256 == 0 and off + slices * p.budget * 4 <= n
+        # it follows the three per-slot score regions
+        assert off >= slices * p.capacity * 4 * 3
+    with pytest.raises(rkv.RkvError):
+        rkv.rkv_workspace_keep_offset(P(capacity=100))
+
+
 BAD_PARAMS = [
     (dict(lam=1.5), "RKV_ERR_BAD_PARAM"),
     (dict(lam=-0.1), "RKV_ERR_BAD_PARAM"),
