@@ -69,7 +69,8 @@ struct Stage {
   static constexpr int SLOTS = RB / 16;                       // 16-byte slots per row
   static constexpr int BYTES = kRowBlock * RB;                // one row block
   static constexpr int PER = BYTES / 1024 / kGramWaves;       // 1 KB direct loads per wave per row block
-  static constexpr int COUNT = sizeof(T) == 2 ? 8 : 3;        // ring depth (LDS: ring + queries <= 160 KB)
+  static constexpr int COUNT = sizeof(T) == 2 ? 7 : 3;        // ring depth (LDS: ring + queries + norms <= 160 KB)
+  static constexpr int NCACHE = sizeof(T) == 2 ? 5120 : 1024; // tokens whose norms stay in LDS after group 0
   static_assert(kRowBlock % kGramWaves == 0 && BYTES % (1024 * kGramWaves) == 0, "row block split");
   static_assert(COUNT >= 3 && COUNT <= 8, "ring depth");
 };
@@ -263,6 +264,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   __shared__ __align__(16) char rows_lds[S::COUNT * S::BYTES];
   __shared__ __align__(16) char q_lds[S::BYTES];               // the slice's query rows
   __shared__ __align__(16) float nrm_lds[S::COUNT][kRowBlock];  // row norms per stage (-1: zero key, 0: past the slice)
+  __shared__ __align__(16) float nrm_all[S::NCACHE];            // the same per token, kept from group 0 on
   __shared__ __align__(16) float rst_lds[RKV_MAX_QROWS * 2];   // per query row: max, 1 / sum of exp
   __shared__ __align__(16) float sv_lds[kHeadDim];             // sum of unit keys
   __shared__ __align__(16) char s_lds[32 * RB];                // s as MFMA rows; scratch before that
@@ -330,12 +332,19 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   float tM[2] = {-INFINITY, -INFINITY}, tS[2] = {0.f, 0.f};  // logit tiles wave and wave + 8
   typename TL::F qtile[2];  // their query fragments (group 0 only), from LDS after the first barrier
   int pg = 0, pbi = 0;  // the pre-pass cursor: block pbi of group pg
+  // row block blk keeps its norms in nrm_all once group 0 has seen it
+  auto cached = [&](int blk) { return (blk + 1) * kRowBlock <= S::NCACHE; };
   // norms of stream block q, and with FIRST (a group-0 block) the statistics
   auto pre = [&](int q, auto first) {
     constexpr bool FIRST = decltype(first)::value;
     const int stg = q % S::COUNT;
     const char* st = rows_lds + stg * S::BYTES;
     const int blk = pg * kGroupBlocks + pbi;  // row block of the slice
+    if (++pbi == nrb - pg * kGroupBlocks) {
+      ++pg;
+      pbi = 0;
+    }
+    if (!FIRST && cached(blk)) return;  // its norms are in LDS since group 0
     float x[16];
     row_chunk16<T>(x, st, pr, pc);
     float ss4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
@@ -343,7 +352,11 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
     for (int e = 0; e < 16; ++e) ss4[e & 3] = fmaf(x[e], x[e], ss4[e & 3]);
     const float nrm = sqrtf(sum8_dpp((ss4[0] + ss4[1]) + (ss4[2] + ss4[3])));  // the row's 8 lanes
     const int j = blk * kRowBlock + pr;  // token of the row
-    if (pc == 0) nrm_lds[stg][pr] = j < N ? (nrm > 0.f ? nrm : -1.f) : 0.f;
+    const float nv = j < N ? (nrm > 0.f ? nrm : -1.f) : 0.f;
+    if (pc == 0) {
+      nrm_lds[stg][pr] = nv;
+      if (FIRST && cached(blk)) nrm_all[j] = nv;
+    }
     if constexpr (FIRST) {
       const float inv = nrm > 0.f ? __builtin_amdgcn_rcpf(nrm) : 0.f;  // rows past the slice are zeros
 #pragma unroll
@@ -381,10 +394,6 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
           tM[u] = Mn;
         }
       }
-    }
-    if (++pbi == nrb - pg * kGroupBlocks) {
-      ++pg;
-      pbi = 0;
     }
   };
 
@@ -425,7 +434,8 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
     if (bi >= wave && cbase < N) {  // row blocks before the wave's own have no pair j > i
       const int stg = q % S::COUNT;
       const char* st = rows_lds + stg * S::BYTES;
-      const float* ns = nrm_lds[stg];
+      const int blk = gg * kGroupBlocks + bi;
+      const float* ns = cached(blk) ? nrm_all + blk * kRowBlock : nrm_lds[stg];
       const bool diag = bi == wave;
       if (diag) {  // the block's rows are the wave's columns
 #pragma unroll

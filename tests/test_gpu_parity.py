@@ -33,6 +33,9 @@ SMALL = {
     "small_a64": synth.small("small_a64", 107, num_layers=1, batch=1, num_kv_heads=2, group=1, budget=320, buffer=50,
                              obs_window=64),
     "single_f32": synth.WORKLOADS["single_f32"],
+    # more tokens than the scoring kernel keeps norms of in LDS: the later
+    # column groups recompute the newest blocks' norms
+    "small_long": synth.small("small_long", 108, num_layers=1, batch=1, num_kv_heads=2, group=4, budget=5600),
 }
 
 # (workload, sampled (layer, sequence, head) slices)
