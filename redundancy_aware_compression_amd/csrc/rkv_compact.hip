@@ -15,8 +15,16 @@
 
 namespace rkv {
 
-constexpr int kCompactThreads = 256;
-constexpr int kCompactUnroll = 8;  // 16-byte loads in flight per thread per chunk
+constexpr int kCompactThreads = 512;
+constexpr int kCompactUnroll = 16;  // 16-byte loads in flight per thread per chunk (128 KB per work-group)
+
+typedef unsigned int u32x4n __attribute__((ext_vector_type(4)));
+
+// The copied rows are not read again by this kernel: both directions bypass
+// the caches' retention (non-temporal), which leaves more of the HBM
+// bandwidth to the streams.
+__device__ inline u32x4n load_nt(const char* p) { return __builtin_nontemporal_load((const u32x4n*)p); }
+__device__ inline void store_nt(char* p, u32x4n v) { __builtin_nontemporal_store(v, (u32x4n*)p); }
 
 template <typename T>
 __global__ __launch_bounds__(kCompactThreads) void compact_kernel(Geom g, LayerPtrs k, LayerPtrs v,
@@ -44,13 +52,13 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(Geom g, LayerP
     seq_start[b] = lo;
   }
 
-  // Eight 16-byte loads per thread per chunk, held in named registers (an
+  // Sixteen 16-byte loads per thread per chunk, held in named registers (an
   // array here is kept in scratch memory across the barrier by the compiler).
-  static_assert(kCompactUnroll == 8, "the chunk body below is written out for 8 loads");
+  static_assert(kCompactUnroll == 16, "the chunk body below is written out for 16 loads");
   for (int c0 = 0; c0 < B; c0 += CH_ROWS) {
-    uint4 v0, v1, v2, v3, v4, v5, v6, v7;
+    u32x4n v0, v1, v2, v3, v4, v5, v6, v7, v8, v9, v10, v11, v12, v13, v14, v15;
     uint32_t mvmask = 0;
-    auto ld = [&](int q, uint4& val) {
+    auto ld = [&](int q, u32x4n& val) {
       const int idx = q * kCompactThreads + tid;
       const int jr = c0 + idx / U4_ROW;
       const int j = min(jr, B - 1), part = idx % U4_ROW;
@@ -58,17 +66,19 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(Geom g, LayerP
       const bool mv = jr < B && src >= 0 && src != j && src < g.n_slots;  // out-of-range sources are ignored
       mvmask |= (uint32_t)mv << q;
       // rows that stay put load their own (in-bounds) bytes and store nothing
-      val = *(const uint4*)(base + (size_t)(mv ? src : j) * RB + part * 16);
+      val = load_nt(base + (size_t)(mv ? src : j) * RB + part * 16);
     };
     ld(0, v0); ld(1, v1); ld(2, v2); ld(3, v3); ld(4, v4); ld(5, v5); ld(6, v6); ld(7, v7);
+    ld(8, v8); ld(9, v9); ld(10, v10); ld(11, v11); ld(12, v12); ld(13, v13); ld(14, v14); ld(15, v15);
     // every source of this chunk is in registers before any row is overwritten
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    auto st = [&](int q, const uint4& val) {
+    auto st = [&](int q, const u32x4n& val) {
       const int idx = q * kCompactThreads + tid;
-      if ((mvmask >> q) & 1u) *(uint4*)(base + (size_t)(c0 + idx / U4_ROW) * RB + (idx % U4_ROW) * 16) = val;
+      if ((mvmask >> q) & 1u) store_nt(base + (size_t)(c0 + idx / U4_ROW) * RB + (idx % U4_ROW) * 16, val);
     };
     st(0, v0); st(1, v1); st(2, v2); st(3, v3); st(4, v4); st(5, v5); st(6, v6); st(7, v7);
+    st(8, v8); st(9, v9); st(10, v10); st(11, v11); st(12, v12); st(13, v13); st(14, v14); st(15, v15);
   }
 }
 
