@@ -185,6 +185,50 @@ rkv_status rkv_evict_step_timed(const rkv_params* p, void* const* k_layers, void
                                 const void* obs_q, int32_t* seq_start, int32_t* n_slots, void* ws, size_t ws_bytes,
                                 void* stream, void* const* stage_events);
 
+/*
+ * Hole-filling layout (order-free compaction with an order sidecar). The
+ * pages name the copy of the kept entries and the re-arrangement of the cache
+ * as costs of pruning (R-KV notes page, Q&A part 2, causes 3 and 4); in this
+ * layout an eviction moves only the kept tokens that arrived since the last
+ * one. Sequence b's valid tokens are the virtual slots [seq_start[b],
+ * n_slots) in age order. Virtual slot v < budget is stored at physical slot
+ * order[slice][v], v >= budget at physical slot v (new tokens are appended
+ * there in order). order is int32 [num_layers][batch][num_kv_heads][budget]
+ * and each slice's row is a permutation of [0, budget); its entries below
+ * seq_start[b] name the free physical slots. The identity permutation turns
+ * a cache laid out for rkv_evict_step into this layout.
+ *
+ * rkv_evict_step_holefill: the eviction of rkv_evict_step (same trigger,
+ * scores and kept set, computed on the virtual order) with the compaction
+ * replaced: kept tokens below the budget stay in their physical slots; the
+ * kept tokens of [budget, n_slots) move, in ascending virtual order, into
+ * the ascending physical slots below the budget that no kept token occupies;
+ * the remaining free slots go, ascending, to the virtual slots before the new
+ * seq_start. order and seq_start are rewritten (in/out), *n_slots becomes
+ * budget. At most n_slots - budget rows of K and of V move per slice. Errors
+ * as rkv_evict_step, plus RKV_ERR_NULL_ARG for a NULL order,
+ * RKV_ERR_MISALIGNED for an order not 4-byte aligned and
+ * RKV_ERR_UNSUPPORTED for a budget above 10,000 (the compaction's LDS). An order row that is
+ * not a permutation gives unspecified slots but no access outside the
+ * slice's rows.
+ */
+rkv_status rkv_evict_step_holefill(const rkv_params* p, void* const* k_layers, void* const* v_layers,
+                                   const void* obs_q, int32_t* seq_start, int32_t* order, int32_t* n_slots, void* ws,
+                                   size_t ws_bytes, void* stream);
+
+/* rkv_evict_step_holefill with the four stage events of rkv_evict_step_timed. */
+rkv_status rkv_evict_step_holefill_timed(const rkv_params* p, void* const* k_layers, void* const* v_layers,
+                                         const void* obs_q, int32_t* seq_start, int32_t* order, int32_t* n_slots,
+                                         void* ws, size_t ws_bytes, void* stream, void* const* stage_events);
+
+/* The compaction of rkv_evict_step_holefill from a given keep list (the
+ * layout of rkv_select's keep: virtual slots, ascending, right-aligned, -1
+ * before the kept entries). keep is read only; order and seq_start are
+ * rewritten. budget <= n_slots <= capacity. */
+rkv_status rkv_compact_holefill(const rkv_params* p, void* const* k_layers, void* const* v_layers,
+                                const int32_t* keep, int32_t* seq_start, int32_t* order, int32_t n_slots,
+                                void* stream);
+
 /* Static string naming a status. */
 const char* rkv_status_string(rkv_status st);
 

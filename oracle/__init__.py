@@ -72,6 +72,9 @@ def load_library(path: str):
     L.orc_gather_rows.restype = None
     L.orc_gather_rows.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_void_p]
+    L.orc_holefill_slice.restype = ctypes.c_int32
+    L.orc_holefill_slice.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     return L
 
 
@@ -177,3 +180,19 @@ def gather_rows(src: np.ndarray, keep: np.ndarray) -> np.ndarray:
     row_bytes = src.strides[0]
     lib().orc_gather_rows(src.ctypes.data, keep.ctypes.data, keep.shape[0], row_bytes, dst.ctypes.data)
     return dst
+
+
+def holefill_slice(K: np.ndarray, V: np.ndarray, order: np.ndarray, keep: np.ndarray, budget: int):
+    """Hole-filling compaction of one slice (orc_holefill_slice) on copies:
+    K, V are the slice's physical rows [n_slots][D], order its budget
+    entries, keep the selection's budget entries. Returns (K', V', order',
+    new start)."""
+    K2, V2 = np.array(K, copy=True, order="C"), np.array(V, copy=True, order="C")
+    o2 = np.array(order, dtype=np.int32, copy=True)
+    kp = np.ascontiguousarray(keep, dtype=np.int32)
+    assert K2.shape == V2.shape and kp.shape[0] == budget and o2.shape[0] == budget
+    lead = lib().orc_holefill_slice(K2.ctypes.data, V2.ctypes.data, K2.strides[0], budget, K2.shape[0],
+                                    kp.ctypes.data, o2.ctypes.data)
+    if lead < 0:
+        raise ValueError("order is not a permutation of [0, budget) or keep is malformed")
+    return K2, V2, o2, int(lead)

@@ -239,3 +239,45 @@ extern "C" int32_t orc_evict_step(const orc_step_params* p, int32_t dtype, void*
   *n_slots = B;
   return 1;
 }
+
+extern "C" int32_t orc_holefill_slice(void* k_rows, void* v_rows, int32_t row_bytes, int32_t budget,
+                                      int32_t n_slots, const int32_t* keep, int32_t* order) {
+  /* [RKV] Q&A part 2, causes 3 and 4: copying the selected KV and
+   * re-arranging the cache are the costs after pruning; this layout copies
+   * only the kept tokens that arrived after the budget. Which free row a
+   * mover takes is a stated choice (ascending to ascending). */
+  const int B = budget;
+  std::vector<int> seen(B, 0);
+  for (int v = 0; v < B; ++v) {
+    if (order[v] < 0 || order[v] >= B || seen[order[v]]) return -1;
+    seen[order[v]] = 1;
+  }
+  int lead = 0;
+  while (lead < B && keep[lead] < 0) ++lead;
+  for (int j = lead; j < B; ++j)
+    if (keep[j] < 0 || keep[j] >= n_slots || (j > lead && keep[j] <= keep[j - 1])) return -1;
+  // rows occupied by the kept tokens that stay
+  std::vector<int> occupied(B, 0);
+  for (int j = lead; j < B; ++j)
+    if (keep[j] < B) occupied[order[keep[j]]] = 1;
+  std::vector<int> free_rows;
+  for (int r = 0; r < B; ++r)
+    if (!occupied[r]) free_rows.push_back(r);
+  std::vector<int> new_order(B, -1);
+  int m = 0;  // movers so far
+  for (int j = lead; j < B; ++j) {
+    if (keep[j] < B) {
+      new_order[j] = order[keep[j]];
+    } else {
+      const int dst = free_rows[m++];
+      std::memcpy((char*)k_rows + (size_t)dst * row_bytes, (const char*)k_rows + (size_t)keep[j] * row_bytes,
+                  (size_t)row_bytes);
+      std::memcpy((char*)v_rows + (size_t)dst * row_bytes, (const char*)v_rows + (size_t)keep[j] * row_bytes,
+                  (size_t)row_bytes);
+      new_order[j] = dst;
+    }
+  }
+  for (int j = 0; j < lead; ++j) new_order[j] = free_rows[m + j];
+  for (int v = 0; v < B; ++v) order[v] = new_order[v];
+  return lead;
+}

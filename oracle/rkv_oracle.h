@@ -87,6 +87,22 @@ int32_t orc_evict_step(const orc_step_params* p, int32_t dtype, void* const* k_l
 /* dst row j <- src row keep[j] for keep[j] >= 0 (out of place). */
 void orc_gather_rows(const void* src, const int32_t* keep, int32_t n_keep, int32_t row_bytes, void* dst);
 
+/*
+ * Hole-filling compaction of one slice (the order-free layout), in place.
+ * The slice's tokens are virtual slots in age order; virtual slot v < budget
+ * is physical row order[v], v >= budget physical row v. keep: budget entries
+ * (virtual slots, ascending, -1 before the kept ones), as the selection
+ * writes them. Kept tokens below the budget stay; the kept tokens at or past
+ * the budget (the movers, ascending) are copied into the physical rows below
+ * the budget that no kept token occupies (the free rows, ascending); the
+ * free rows left over go, ascending, to the virtual slots before the new
+ * start. k_rows, v_rows: the slice's n_slots physical rows of row_bytes each.
+ * Returns the new start (number of -1 entries) or -1 if order is not a
+ * permutation of [0, budget) or keep is malformed.
+ */
+int32_t orc_holefill_slice(void* k_rows, void* v_rows, int32_t row_bytes, int32_t budget, int32_t n_slots,
+                           const int32_t* keep, int32_t* order);
+
 #ifdef __cplusplus
 }
 #endif

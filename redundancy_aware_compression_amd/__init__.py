@@ -22,7 +22,10 @@ from ._binding import (  # noqa: F401
     library_path,
     make_params,
     rkv_compact,
+    rkv_compact_holefill,
     rkv_evict_step,
+    rkv_evict_step_holefill,
+    rkv_evict_step_holefill_timed,
     rkv_evict_step_timed,
     rkv_last_hip_error,
     rkv_score,

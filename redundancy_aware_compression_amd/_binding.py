@@ -90,6 +90,12 @@ def _lib():
         L.rkv_evict_step.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(i32), vp, sz, vp]
         L.rkv_evict_step_timed.restype = ctypes.c_int
         L.rkv_evict_step_timed.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(i32), vp, sz, vp, vp]
+        L.rkv_evict_step_holefill.restype = ctypes.c_int
+        L.rkv_evict_step_holefill.argtypes = [P, vp, vp, vp, vp, vp, ctypes.POINTER(i32), vp, sz, vp]
+        L.rkv_evict_step_holefill_timed.restype = ctypes.c_int
+        L.rkv_evict_step_holefill_timed.argtypes = [P, vp, vp, vp, vp, vp, ctypes.POINTER(i32), vp, sz, vp, vp]
+        L.rkv_compact_holefill.restype = ctypes.c_int
+        L.rkv_compact_holefill.argtypes = [P, vp, vp, vp, vp, vp, i32, vp]
         L.rkv_status_string.restype = ctypes.c_char_p
         L.rkv_status_string.argtypes = [ctypes.c_int]
         L.rkv_last_hip_error.restype = ctypes.c_int
@@ -195,3 +201,41 @@ def rkv_evict_step_timed(p: RkvParams, k_layers: Sequence, v_layers: Sequence, o
     if check:
         _check(st, "rkv_evict_step_timed")
     return st, ns.value
+
+
+def rkv_evict_step_holefill(p: RkvParams, k_layers: Sequence, v_layers: Sequence, obs_q, seq_start, order,
+                            n_slots: int, ws, ws_bytes: int, stream=None, check: bool = True):
+    """The eviction step in the hole-filling layout; returns (status, n_slots after the step)."""
+    ns = ctypes.c_int32(n_slots)
+    st = _lib().rkv_evict_step_holefill(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
+                                        ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(obs_q),
+                                        _ptr(seq_start), _ptr(order), ctypes.byref(ns), _ptr(ws), ws_bytes,
+                                        _stream(stream))
+    if check:
+        _check(st, "rkv_evict_step_holefill")
+    return st, ns.value
+
+
+def rkv_evict_step_holefill_timed(p: RkvParams, k_layers: Sequence, v_layers: Sequence, obs_q, seq_start, order,
+                                  n_slots: int, ws, ws_bytes: int, stage_events: Sequence[int], stream=None,
+                                  check: bool = True):
+    """rkv_evict_step_holefill recording 4 caller-created hipEvent_t handles between its stages."""
+    ns = ctypes.c_int32(n_slots)
+    if len(stage_events) != 4:
+        raise ValueError("rkv_evict_step_holefill_timed takes 4 events")
+    ev = (ctypes.c_void_p * 4)(*stage_events)
+    st = _lib().rkv_evict_step_holefill_timed(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
+                                              ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(obs_q),
+                                              _ptr(seq_start), _ptr(order), ctypes.byref(ns), _ptr(ws), ws_bytes,
+                                              _stream(stream), ctypes.cast(ev, ctypes.c_void_p))
+    if check:
+        _check(st, "rkv_evict_step_holefill_timed")
+    return st, ns.value
+
+
+def rkv_compact_holefill(p: RkvParams, k_layers: Sequence, v_layers: Sequence, keep, seq_start, order,
+                         n_slots: int, stream=None, check: bool = True) -> int:
+    st = _lib().rkv_compact_holefill(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
+                                     ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(keep),
+                                     _ptr(seq_start), _ptr(order), n_slots, _stream(stream))
+    return _check(st, "rkv_compact_holefill") if check else st

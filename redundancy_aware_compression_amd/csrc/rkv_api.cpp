@@ -123,7 +123,7 @@ rkv_status rkv_score(const rkv_params* p, const void* const* k_layers, const voi
   const rkv::Geom g = make_geom(p, n_slots);
   const rkv::LayerPtrs kl = make_layers(p, k_layers);
   int32_t* cnt = counts ? counts : w.counts;
-  RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, importance, w.rowmean, cnt, stream));
+  RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, nullptr, importance, w.rowmean, cnt, stream));
   RKV_TRY(rkv::launch_redundancy(g, seq_start, cnt, w.rowmean, redundancy, stream));
   return RKV_OK;
 }
@@ -154,15 +154,22 @@ rkv_status rkv_compact(const rkv_params* p, void* const* k_layers, void* const* 
   return RKV_OK;
 }
 
-rkv_status rkv_evict_step_timed(const rkv_params* p, void* const* k_layers, void* const* v_layers,
-                                const void* obs_q, int32_t* seq_start, int32_t* n_slots, void* ws, size_t ws_bytes,
-                                void* stream, void* const* stage_events) {
+}  // extern "C"
+
+namespace {
+
+// The eviction step; with `order` the hole-filling layout (gathered scoring
+// loads, hole-filling compaction), else the order-preserving one.
+rkv_status evict_impl(const rkv_params* p, void* const* k_layers, void* const* v_layers, const void* obs_q,
+                      int32_t* seq_start, int32_t* order, bool holefill, int32_t* n_slots, void* ws, size_t ws_bytes,
+                      void* stream, void* const* stage_events) {
   rkv_status st = check_params(p);
   if (st != RKV_OK) return st;
   if ((st = check_layers(p, (const void* const*)k_layers)) != RKV_OK) return st;
   if ((st = check_layers(p, (const void* const*)v_layers)) != RKV_OK) return st;
-  if (!obs_q || !seq_start || !n_slots || !ws) return RKV_ERR_NULL_ARG;
-  if (!aligned16(obs_q) || ((uintptr_t)ws & 255u)) return RKV_ERR_MISALIGNED;
+  if (!obs_q || !seq_start || !n_slots || !ws || (holefill && !order)) return RKV_ERR_NULL_ARG;
+  if (holefill && rkv::holefill_lds_bytes(p->budget) > rkv::kHolefillMaxLds) return RKV_ERR_UNSUPPORTED;
+  if (!aligned16(obs_q) || ((uintptr_t)ws & 255u) || ((uintptr_t)order & 3u)) return RKV_ERR_MISALIGNED;
   const int32_t ns = *n_slots;
   if (ns < 0 || ns > p->capacity) return RKV_ERR_BAD_SHAPE;
   rkv::Workspace w = rkv::carve(*p, ws);
@@ -177,20 +184,65 @@ rkv_status rkv_evict_step_timed(const rkv_params* p, void* const* k_layers, void
     return (int)hipEventRecord((hipEvent_t)stage_events[i], (hipStream_t)stream);
   };
   RKV_TRY(mark(0));
-  RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, w.importance, w.rowmean, w.counts, stream));
+  RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, holefill ? order : nullptr, w.importance, w.rowmean,
+                           w.counts, stream));
   RKV_TRY(mark(1));
   RKV_TRY(rkv::launch_select(g, w.importance, nullptr, w.counts, w.rowmean, seq_start, w.keep, nullptr, nullptr,
                              stream));
   RKV_TRY(mark(2));
-  RKV_TRY(rkv::launch_compact(g, p->dtype, kl, vl, w.keep, seq_start, stream));
+  if (holefill)
+    RKV_TRY(rkv::launch_compact_holefill(g, p->dtype, kl, vl, w.keep, order, seq_start, stream));
+  else
+    RKV_TRY(rkv::launch_compact(g, p->dtype, kl, vl, w.keep, seq_start, stream));
   RKV_TRY(mark(3));
   *n_slots = p->budget;
   return RKV_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+rkv_status rkv_evict_step_timed(const rkv_params* p, void* const* k_layers, void* const* v_layers,
+                                const void* obs_q, int32_t* seq_start, int32_t* n_slots, void* ws, size_t ws_bytes,
+                                void* stream, void* const* stage_events) {
+  return evict_impl(p, k_layers, v_layers, obs_q, seq_start, nullptr, false, n_slots, ws, ws_bytes, stream,
+                    stage_events);
+}
+
 rkv_status rkv_evict_step(const rkv_params* p, void* const* k_layers, void* const* v_layers, const void* obs_q,
                           int32_t* seq_start, int32_t* n_slots, void* ws, size_t ws_bytes, void* stream) {
-  return rkv_evict_step_timed(p, k_layers, v_layers, obs_q, seq_start, n_slots, ws, ws_bytes, stream, nullptr);
+  return evict_impl(p, k_layers, v_layers, obs_q, seq_start, nullptr, false, n_slots, ws, ws_bytes, stream, nullptr);
+}
+
+rkv_status rkv_evict_step_holefill(const rkv_params* p, void* const* k_layers, void* const* v_layers,
+                                   const void* obs_q, int32_t* seq_start, int32_t* order, int32_t* n_slots, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  return evict_impl(p, k_layers, v_layers, obs_q, seq_start, order, true, n_slots, ws, ws_bytes, stream, nullptr);
+}
+
+rkv_status rkv_evict_step_holefill_timed(const rkv_params* p, void* const* k_layers, void* const* v_layers,
+                                         const void* obs_q, int32_t* seq_start, int32_t* order, int32_t* n_slots,
+                                         void* ws, size_t ws_bytes, void* stream, void* const* stage_events) {
+  return evict_impl(p, k_layers, v_layers, obs_q, seq_start, order, true, n_slots, ws, ws_bytes, stream,
+                    stage_events);
+}
+
+rkv_status rkv_compact_holefill(const rkv_params* p, void* const* k_layers, void* const* v_layers,
+                                const int32_t* keep, int32_t* seq_start, int32_t* order, int32_t n_slots,
+                                void* stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  if ((st = check_layers(p, (const void* const*)k_layers)) != RKV_OK) return st;
+  if ((st = check_layers(p, (const void* const*)v_layers)) != RKV_OK) return st;
+  if (!keep || !seq_start || !order) return RKV_ERR_NULL_ARG;
+  if (rkv::holefill_lds_bytes(p->budget) > rkv::kHolefillMaxLds) return RKV_ERR_UNSUPPORTED;
+  if ((uintptr_t)order & 3u) return RKV_ERR_MISALIGNED;
+  if (n_slots < p->budget || n_slots > p->capacity) return RKV_ERR_BAD_SHAPE;
+  const rkv::Geom g = make_geom(p, n_slots);
+  RKV_TRY(rkv::launch_compact_holefill(g, p->dtype, make_layers(p, (const void* const*)k_layers),
+                                       make_layers(p, (const void* const*)v_layers), keep, order, seq_start, stream));
+  return RKV_OK;
 }
 
 }  // extern "C"

@@ -82,6 +82,156 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(Geom g, LayerP
   }
 }
 
+// ---------------------------------------------------------------------------
+// Hole-filling compaction (order-free): the slice's tokens are virtual slots
+// [s0, n_slots) in age order; virtual slot v < budget lives at physical slot
+// order[v], v >= budget at v, and order[0 .. budget) is a permutation of the
+// physical slots [0, budget) (entries below s0 name the free ones). After
+// selection the kept tokens that already lie below the budget stay where
+// they are; only the kept tokens of [budget, n_slots) move, into the
+// physical slots below the budget that no kept token occupies (ascending
+// movers into ascending free slots); the remaining free slots go, in
+// ascending order, to the virtual slots before the new s0. The rows moved
+// per slice are at most n_slots - budget, instead of about budget for the
+// order-preserving compaction (R-KV notes page, Q&A part 2, causes 3 and 4:
+// copying the selected KV and re-arranging the cache are the costs after
+// pruning). One work-group per slice; LDS holds the keep list, the old order
+// and the free list as 16-bit slots and a bitmap of occupied slots.
+constexpr int kHoleThreads = 256;
+
+__device__ inline int block_sum_hole(int v, int* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  v = wave_sum_i(v);
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int i = 0; i < kHoleThreads / 64; ++i) t += red[i];
+  __syncthreads();
+  return t;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kHoleThreads) void holefill_kernel(Geom g, LayerPtrs k, LayerPtrs v,
+                                                                const int32_t* __restrict__ keep,
+                                                                int32_t* __restrict__ order,
+                                                                int32_t* __restrict__ seq_start) {
+  constexpr int RB = kHeadDim * Elem<T>::kBytes;
+  constexpr int U4_ROW = RB / 16;
+  extern __shared__ __align__(16) char hole_lds[];
+  const int B = g.budget, tid = threadIdx.x;
+  const int nwords = (B + 31) / 32;
+  uint16_t* kl = (uint16_t*)hole_lds;  // keep list (0xFFFF: none)
+  uint16_t* ol = kl + B;               // old order
+  uint16_t* fl = ol + B;               // free physical slots, ascending
+  uint32_t* used = (uint32_t*)(hole_lds + ((6 * (size_t)B + 15) & ~(size_t)15));
+  __shared__ int red[kHoleThreads / 64];
+  __shared__ int scan[kHoleThreads];
+
+  const int slice = xcd_remap(blockIdx.x, gridDim.x);
+  int l, b, h;
+  slice_coords(g, slice, l, b, h);
+  const int32_t* krow = keep + (size_t)slice * B;
+  int32_t* orow = order + (size_t)slice * B;
+
+  // 1. the keep list (virtual slots, ascending after the leading -1) and the old order
+  int nlead = 0, nstay = 0;
+  for (int j = tid; j < B; j += kHoleThreads) {
+    const int kv = krow[j], o = orow[j];
+    const bool valid = kv >= 0 && kv < g.n_slots;
+    kl[j] = valid ? (uint16_t)kv : (uint16_t)0xFFFF;
+    ol[j] = (uint16_t)(o >= 0 && o < B ? o : 0xFFFF);
+    nlead += kv < 0 ? 1 : 0;
+    nstay += valid && kv < B ? 1 : 0;
+  }
+  for (int w = tid; w < nwords; w += kHoleThreads) used[w] = 0u;
+  nlead = block_sum_hole(nlead, red);  // new first valid virtual slot
+  nstay = block_sum_hole(nstay, red);  // kept tokens already below the budget
+  // 2. physical slots of the kept tokens that stay
+  for (int j = tid; j < B; j += kHoleThreads) {
+    const int kv = kl[j];
+    if (kv != 0xFFFF && kv < B && ol[kv] != 0xFFFF) atomicOr(&used[ol[kv] >> 5], 1u << (ol[kv] & 31));
+  }
+  __syncthreads();
+  // 3. free slots, ascending: per word counts, a block scan, then the slots
+  const int per = (nwords + kHoleThreads - 1) / kHoleThreads;  // words per thread
+  int cnt = 0;
+  for (int w = tid * per; w < min(nwords, (tid + 1) * per); ++w) {
+    const uint32_t valid = w == nwords - 1 && (B & 31) ? (1u << (B & 31)) - 1u : 0xFFFFFFFFu;
+    cnt += __popc(~used[w] & valid);
+  }
+  scan[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < kHoleThreads; off <<= 1) {  // inclusive scan
+    const int add = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  const int nfree = scan[kHoleThreads - 1];
+  int rank = scan[tid] - cnt;
+  for (int w = tid * per; w < min(nwords, (tid + 1) * per); ++w) {
+    const uint32_t valid = w == nwords - 1 && (B & 31) ? (1u << (B & 31)) - 1u : 0xFFFFFFFFu;
+    uint32_t f = ~used[w] & valid;
+    while (f) {
+      const int bit = __ffs(f) - 1;
+      f &= f - 1;
+      fl[rank++] = (uint16_t)(32 * w + bit);
+    }
+  }
+  __syncthreads();
+  // 4. the new order: stayers keep their slot, movers (the kept tokens past
+  // the budget, a suffix of the keep list) take the first free slots, the
+  // virtual slots before the new start the rest
+  const int j0 = nlead + nstay;  // first mover
+  const int nmov = B - j0;
+  for (int j = tid; j < B; j += kHoleThreads) {
+    int o;
+    if (j < nlead) {
+      const int r = nmov + j;
+      o = r < nfree ? fl[r] : 0;
+    } else if (j < j0) {
+      const int kv = kl[j];
+      o = kv != 0xFFFF && ol[kv] != 0xFFFF ? ol[kv] : 0;
+    } else {
+      const int r = j - j0;
+      o = r < nfree ? fl[r] : 0;
+    }
+    orow[j] = o;
+  }
+  // 5. move the rows of K and V: sources at or past the budget, destinations
+  // below it, so no row is both read and written
+  const size_t sbase = ((size_t)b * g.H + h) * g.capacity * (size_t)RB;
+  char* kb = (char*)k.p[l] + sbase;
+  char* vb = (char*)v.p[l] + sbase;
+  for (int idx = tid; idx < 2 * nmov * U4_ROW; idx += kHoleThreads) {
+    const int kvsel = idx / (nmov * U4_ROW), rem = idx % (nmov * U4_ROW);
+    const int m = rem / U4_ROW, part = rem % U4_ROW;
+    const int src = kl[j0 + m];
+    if (m >= nfree || src == 0xFFFF || src < B) continue;
+    char* base = kvsel ? vb : kb;
+    store_nt(base + (size_t)fl[m] * RB + part * 16, load_nt(base + (size_t)src * RB + part * 16));
+  }
+  if (l == 0 && h == 0 && tid == 0) seq_start[b] = nlead;
+}
+
+size_t holefill_lds_bytes(int budget) { return ((6 * (size_t)budget + 15) & ~(size_t)15) + 4 * (size_t)((budget + 31) / 32); }
+
+int launch_compact_holefill(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const int32_t* keep,
+                            int32_t* order, int32_t* seq_start, void* stream) {
+  const int slices = g.L * g.batch * g.H;
+  if (slices == 0) return 0;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t lds = holefill_lds_bytes(g.budget);
+  if (dtype == RKV_BF16)
+    hipLaunchKernelGGL(holefill_kernel<bf16_t>, dim3(slices), dim3(kHoleThreads), lds, s, g, k, v, keep, order,
+                       seq_start);
+  else
+    hipLaunchKernelGGL(holefill_kernel<float>, dim3(slices), dim3(kHoleThreads), lds, s, g, k, v, keep, order,
+                       seq_start);
+  return (int)hipGetLastError();
+}
+
 int launch_compact(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const int32_t* keep,
                    int32_t* seq_start, void* stream) {
   const int slices = g.L * g.batch * g.H;

@@ -252,9 +252,14 @@ struct SRows<float> {
   __device__ static float dot(const f32x16& acc) { return acc[0]; }
 };
 
-template <typename T>
+// GATHER: the slice's valid tokens are virtual slots [s0, n_slots); virtual
+// slot v < budget is stored at physical slot order[v], v >= budget at v (the
+// layout the hole-filling compaction keeps). The row loads gather physical
+// rows in virtual order; everything else works in virtual slots.
+template <typename T, bool GATHER>
 __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k, const void* __restrict__ obs_q,
                                                             const int32_t* __restrict__ seq_start,
+                                                            const int32_t* __restrict__ order,
                                                             float* __restrict__ importance,
                                                             float* __restrict__ rowmean, int32_t* __restrict__ counts) {
   using S = Stage<T>;
@@ -284,30 +289,82 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   // every group's row blocks in one stream: group gg contributes nrb - 8 gg
   const int total = ngroups * nrb - kGroupBlocks * ngroups * (ngroups - 1) / 2;
 
-  // the slice's valid rows as a range-checked buffer
-  const u32x4_t rk = make_desc(row_ptr<T>(k.p[l], g, b, h, s0), (uint32_t)N * RB);
+  // the slice's valid rows (GATHER: all its physical rows below n_slots) as a
+  // range-checked buffer
+  const u32x4_t rk = GATHER ? make_desc(row_ptr<T>(k.p[l], g, b, h, 0), (uint32_t)g.n_slots * RB)
+                            : make_desc(row_ptr<T>(k.p[l], g, b, h, s0), (uint32_t)N * RB);
   const uint32_t ring = lds_addr(rows_lds);
 
-  // block-invariant per-lane offsets of the row-block loads
-  uint32_t voff[S::PER];
+  // block-invariant per-lane offsets of the row-block loads: load q of a
+  // wave brings row r = 8 wave + (64 q + lane) / SLOTS of the block, bytes
+  // 16 (p ^ (r & 15)) .. of it (vpart)
+  static_assert(S::PER * 64 / S::SLOTS * kGramWaves == kRowBlock, "each wave loads 8 whole rows");
+  constexpr int KPQ = 64 / S::SLOTS;  // rows per load
+  uint32_t voff[S::PER], vpart[S::PER];
 #pragma unroll
   for (int q = 0; q < S::PER; ++q) {
     const int flat = (wave * S::PER + q) * 64 + lane;
     const int r = flat / S::SLOTS, p = flat % S::SLOTS;
-    voff[q] = (uint32_t)r * RB + (uint32_t)(p ^ (r & 15)) * 16;
+    vpart[q] = (uint32_t)(p ^ (r & 15)) * 16;
+    voff[q] = (uint32_t)r * RB + vpart[q];
   }
 
   // ---- loads: the first row block, the queries (all waves), the rest of
   // the ring; the issue cursor walks the stream (block ibi of group ig)
   int ig = 0, ibi = 0;
+  // GATHER: physical slots of the wave's 8 rows of the cursor's block, read
+  // (scalar loads) one issue ahead; rows past the slice point past the buffer
+  // (eight named scalars: an array here ends up in scratch memory, whose
+  // accesses would count among the ring's vmcnt)
+  int on0 = 0, on1 = 0, on2 = 0, on3 = 0, on4 = 0, on5 = 0, on6 = 0, on7 = 0;
+  const int32_t* ord = GATHER ? order + (size_t)slice * g.budget : nullptr;
+  auto fetch_order = [&]() {
+    if constexpr (GATHER) {
+      const int vb = s0 + (ig * kGroupBlocks + ibi) * kRowBlock + 8 * wave;  // virtual slot of row 8 wave
+      auto phys_of = [&](int v) {
+        const int o = ord[min(v, g.budget - 1)];
+        return __builtin_amdgcn_readfirstlane(v < g.budget ? o : (v < g.n_slots ? v : g.n_slots));
+      };
+      on0 = phys_of(vb + 0);
+      on1 = phys_of(vb + 1);
+      on2 = phys_of(vb + 2);
+      on3 = phys_of(vb + 3);
+      on4 = phys_of(vb + 4);
+      on5 = phys_of(vb + 5);
+      on6 = phys_of(vb + 6);
+      on7 = phys_of(vb + 7);
+    }
+  };
+  // physical slot of the lane's row in load qq (row 8 wave + KPQ qq + lane / SLOTS)
+  auto lane_phys = [&](int qq) {
+    const int li = lane / S::SLOTS;
+    if constexpr (KPQ == 4) {
+      const int a = qq == 0 ? on0 : on4, b2 = qq == 0 ? on1 : on5, c = qq == 0 ? on2 : on6, d = qq == 0 ? on3 : on7;
+      return li == 0 ? a : li == 1 ? b2 : li == 2 ? c : d;
+    } else {
+      static_assert(KPQ == 2, "bf16 or fp32 rows");
+      const int a = qq == 0 ? on0 : qq == 1 ? on2 : qq == 2 ? on4 : on6;
+      const int b2 = qq == 0 ? on1 : qq == 1 ? on3 : qq == 2 ? on5 : on7;
+      return li == 0 ? a : b2;
+    }
+  };
   auto issue_next = [&](int q) {  // stream block q (the cursor's block) into stage q % COUNT
     const int rbase = (ig * kGroupBlocks + ibi) * kRowBlock;
-    issue_rows<T>(ring + (q % S::COUNT) * S::BYTES, rk, voff, (uint32_t)rbase * RB, wave);
+    if constexpr (GATHER) {
+      uint32_t off[S::PER];
+#pragma unroll
+      for (int qq = 0; qq < S::PER; ++qq) off[qq] = (uint32_t)lane_phys(qq) * RB + vpart[qq];
+      issue_rows<T>(ring + (q % S::COUNT) * S::BYTES, rk, off, 0u, wave);
+    } else {
+      issue_rows<T>(ring + (q % S::COUNT) * S::BYTES, rk, voff, (uint32_t)rbase * RB, wave);
+    }
     if (++ibi == nrb - ig * kGroupBlocks) {
       ++ig;
       ibi = 0;
     }
+    fetch_order();
   };
+  fetch_order();
   issue_next(0);
   issue_rows<T>(lds_addr(q_lds),
                 make_desc((const char*)obs_q + ((size_t)(l * g.batch + b) * g.H + h) * (size_t)g.qrows * RB,
@@ -716,16 +773,26 @@ __global__ void redundancy_kernel(Geom g, const int32_t* __restrict__ seq_start,
 }
 
 int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q, const int32_t* seq_start,
-                float* importance, float* rowmean, int32_t* counts, void* stream) {
+                const int32_t* order, float* importance, float* rowmean, int32_t* counts, void* stream) {
   const int slices = g.L * g.batch * g.H;
   if (slices == 0) return 0;
   hipStream_t s = (hipStream_t)stream;
-  if (dtype == RKV_BF16)
-    hipLaunchKernelGGL(gram_kernel<bf16_t>, dim3(slices), dim3(kGramThreads), 0, s, g, k, obs_q, seq_start,
-                       importance, rowmean, counts);
-  else
-    hipLaunchKernelGGL(gram_kernel<float>, dim3(slices), dim3(kGramThreads), 0, s, g, k, obs_q, seq_start,
-                       importance, rowmean, counts);
+  const dim3 grid(slices), block(kGramThreads);
+  if (dtype == RKV_BF16) {
+    if (order)
+      hipLaunchKernelGGL((gram_kernel<bf16_t, true>), grid, block, 0, s, g, k, obs_q, seq_start, order, importance,
+                         rowmean, counts);
+    else
+      hipLaunchKernelGGL((gram_kernel<bf16_t, false>), grid, block, 0, s, g, k, obs_q, seq_start, order, importance,
+                         rowmean, counts);
+  } else {
+    if (order)
+      hipLaunchKernelGGL((gram_kernel<float, true>), grid, block, 0, s, g, k, obs_q, seq_start, order, importance,
+                         rowmean, counts);
+    else
+      hipLaunchKernelGGL((gram_kernel<float, false>), grid, block, 0, s, g, k, obs_q, seq_start, order, importance,
+                         rowmean, counts);
+  }
   return (int)hipGetLastError();
 }
 

@@ -73,12 +73,17 @@ inline Workspace carve(const rkv_params& p, void* base) {
 // Kernel launchers (one translation unit each). They return the hipError_t
 // of the launch as an int (0 = success).
 int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q, const int32_t* seq_start,
-                float* importance, float* rowmean, int32_t* counts, void* stream);
+                const int32_t* order, float* importance, float* rowmean, int32_t* counts, void* stream);
 int launch_redundancy(const Geom& g, const int32_t* seq_start, const int32_t* counts, const float* rowmean,
                       float* redundancy, void* stream);
 int launch_select(const Geom& g, const float* importance, const float* redundancy, const int32_t* counts,
                   const float* rowmean, const int32_t* seq_start, int32_t* keep, float* z_out, float* r_out,
                   void* stream);
+// dynamic LDS of the hole-filling compaction; launches keep it within 64 KB
+size_t holefill_lds_bytes(int budget);
+constexpr size_t kHolefillMaxLds = 65536 - 2048;
+int launch_compact_holefill(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const int32_t* keep,
+                            int32_t* order, int32_t* seq_start, void* stream);
 int launch_compact(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const int32_t* keep,
                    int32_t* seq_start, void* stream);
 

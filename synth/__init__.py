@@ -465,9 +465,12 @@ class DeviceSweep:
     `budget` slots (the repeats' windows are read from the device cache) and
     leaves n_slots = budget + buffer with every sequence starting at slot 0.
     The caller then runs the eviction step, which must bring n_slots back to
-    `budget`."""
+    `budget`. With order=True the cache is kept in the hole-filling layout:
+    `order` [L][b][H][budget] int32 (identity at first) maps the retained
+    virtual slots to physical rows, and the repeats read their windows
+    through it."""
 
-    def __init__(self, sweep: Sweep, device="cuda"):
+    def __init__(self, sweep: Sweep, device="cuda", order: bool = False):
         import torch
 
         self.torch, self.sweep, self.w = torch, sweep, sweep.w
@@ -480,6 +483,10 @@ class DeviceSweep:
         del cs
         self.seq_start = torch.zeros(w.batch, dtype=torch.int32, device=self.dev)
         self.n_slots = w.budget
+        self.order = None
+        if order:
+            ident = torch.arange(w.budget, dtype=torch.int32, device=self.dev)
+            self.order = ident.repeat(w.slices).view(w.num_layers, w.batch, w.num_kv_heads, w.budget).contiguous()
 
     def _up(self, a: np.ndarray):
         t = self.torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
@@ -500,6 +507,9 @@ class DeviceSweep:
         assert self.n_slots == w.budget, "the previous round was not evicted"
         rnd = self.sweep.begin_round(r)
         rows = torch.from_numpy(rnd.window_rows(w)).to(self.dev)
+        if self.order is not None:  # virtual retained slots -> physical rows
+            sl, v = rows // w.capacity, rows % w.capacity
+            rows = sl * w.capacity + self.order.view(-1, w.budget)[sl, v].long()
         win = self.host(self.K.view(-1, w.head_dim).index_select(0, rows))
         self.sweep.finish_round(rnd, win)
         B, n = w.budget, w.buffer

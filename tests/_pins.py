@@ -304,6 +304,79 @@ def check_step_noop_and_compaction():
                 assert np.array_equal(K1[l, b, h, w.n_slots:].view(np.uint16), c.K[l, b, h, w.n_slots:].view(np.uint16))
 
 
+HOLEFILL = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "holefill_cases.json")
+
+
+def holefill_cases():
+    with open(HOLEFILL) as f:
+        return json.load(f)["cases"]
+
+
+def check_holefill_hand_cases():
+    """Hole-filling compaction: the hand-derived cases (physical row p holds
+    the value p; every row is 2 values wide, K and V alike)."""
+    for c in holefill_cases():
+        n, B = c["n_slots"], c["budget"]
+        K = np.repeat(np.arange(n, dtype=np.float32)[:, None], 2, axis=1)
+        V = K + 1000.0
+        K2, V2, o2, lead = oracle.holefill_slice(K, V, np.array(c["order"]), np.array(c["keep"]), B)
+        assert lead == c["start_after"], (c["name"], lead)
+        assert o2.tolist() == c["order_after"], (c["name"], o2.tolist())
+        assert K2[:, 0].tolist() == c["rows_after"], (c["name"], K2[:, 0].tolist())
+        assert (V2[:, 0] - 1000.0).tolist() == c["rows_after"], c["name"]
+
+
+def _rand_holefill(rng, B, n_slots, n_valid, n_keep):
+    """A random permutation order and a valid ascending keep list of n_keep
+    virtual slots among the n_valid newest (right-aligned, -1 before)."""
+    order = rng.permutation(B).astype(np.int32)
+    s0 = n_slots - n_valid
+    kept = np.sort(rng.choice(np.arange(s0, n_slots), size=n_keep, replace=False)).astype(np.int32)
+    keep = np.full(B, -1, np.int32)
+    keep[B - n_keep:] = kept
+    return order, keep
+
+
+def check_holefill_invariants():
+    """Random cases: the new order is a permutation; every kept token's row is
+    found at its new physical row; kept tokens below the budget did not move;
+    only rows that received a mover changed, at most n_slots - budget of them."""
+    rng = np.random.default_rng(7)
+    for _ in range(200):
+        B = int(rng.integers(2, 40))
+        buf = int(rng.integers(1, 20))
+        n = B + buf
+        n_valid = int(rng.integers(1, n + 1))
+        n_keep = min(n_valid, B)
+        order, keep = _rand_holefill(rng, B, n, n_valid, n_keep)
+        K = rng.standard_normal((n, 3)).astype(np.float32)
+        V = rng.standard_normal((n, 3)).astype(np.float32)
+        virt = lambda X, v: X[order[v]] if v < B else X[v]
+        K2, V2, o2, lead = oracle.holefill_slice(K, V, order, keep, B)
+        assert lead == B - n_keep
+        assert sorted(o2.tolist()) == list(range(B))
+        for j in range(lead, B):
+            assert np.array_equal(K2[o2[j]], virt(K, keep[j])) and np.array_equal(V2[o2[j]], virt(V, keep[j]))
+            if keep[j] < B:
+                assert o2[j] == order[keep[j]]
+        changed = [r for r in range(n) if not np.array_equal(K2[r], K[r])]
+        movers = int((keep >= B).sum())
+        assert len(changed) <= movers <= buf
+        assert all(r < B for r in changed)
+        assert np.array_equal(K2[B:], K[B:])
+
+
+def check_holefill_rejects_bad_order():
+    """An order row that is not a permutation is refused."""
+    K = np.zeros((6, 2), np.float32)
+    for bad in ([0, 0, 1, 2], [0, 1, 2, 4], [-1, 1, 2, 3]):
+        try:
+            oracle.holefill_slice(K, K, np.array(bad), np.array([0, 1, 2, 3]), 4)
+        except ValueError:
+            continue
+        raise AssertionError(f"accepted {bad}")
+
+
 ALL_CHECKS = [
     check_hand_cases,
     check_lambda1_textbook,
@@ -317,4 +390,7 @@ ALL_CHECKS = [
     check_bruteforce_topk,
     check_lambda0_least_redundant,
     check_step_noop_and_compaction,
+    check_holefill_hand_cases,
+    check_holefill_invariants,
+    check_holefill_rejects_bad_order,
 ]

@@ -110,6 +110,35 @@ def test_bad_params_rejected_by_every_entry_point(kw, expect):
     assert rkv.rkv_compact(p, layers(), layers(), FAKE, FAKE, 300, stream=0, check=False) == code
     st, ns = rkv.rkv_evict_step(p, layers(), layers(), FAKE, FAKE, 384, FAKE_WS, 1 << 40, stream=0, check=False)
     assert st == code and ns == 384
+    st, ns = rkv.rkv_evict_step_holefill(p, layers(), layers(), FAKE, FAKE, FAKE, 384, FAKE_WS, 1 << 40, stream=0,
+                                         check=False)
+    assert st == code and ns == 384
+    assert rkv.rkv_compact_holefill(p, layers(), layers(), FAKE, FAKE, FAKE, 300, stream=0, check=False) == code
+
+
+def test_holefill_argument_errors():
+    """The hole-filling entry points: NULL or misaligned order, slot range,
+    and the no-op below the trigger (nothing launched, fake pointers untouched)."""
+    p = P()
+    need = rkv.rkv_workspace_bytes(p)
+    NULL, MIS, SHAPE = st_of("RKV_ERR_NULL_ARG"), st_of("RKV_ERR_MISALIGNED"), st_of("RKV_ERR_BAD_SHAPE")
+    st, _ = rkv.rkv_evict_step_holefill(p, layers(), layers(), FAKE, FAKE, 0, 384, FAKE_WS, need, stream=0,
+                                        check=False)
+    assert st == NULL
+    st, _ = rkv.rkv_evict_step_holefill(p, layers(), layers(), FAKE, FAKE, FAKE + 2, 384, FAKE_WS, need, stream=0,
+                                        check=False)
+    assert st == MIS
+    assert rkv.rkv_compact_holefill(p, layers(), layers(), FAKE, FAKE, 0, 300, stream=0, check=False) == NULL
+    assert rkv.rkv_compact_holefill(p, layers(), layers(), FAKE, FAKE, FAKE + 1, 300, stream=0, check=False) == MIS
+    assert rkv.rkv_compact_holefill(p, layers(), layers(), FAKE, FAKE, FAKE, 255, stream=0, check=False) == SHAPE
+    big = P(budget=12000, capacity=12200)
+    st, _ = rkv.rkv_evict_step_holefill(big, layers(), layers(), FAKE, FAKE, FAKE, 12200, FAKE_WS, 1 << 40,
+                                        stream=0, check=False)
+    assert st == st_of("RKV_ERR_UNSUPPORTED")
+    for ns in (0, 255, 383):
+        st, out = rkv.rkv_evict_step_holefill(p, layers(), layers(), FAKE, FAKE, FAKE, ns, FAKE_WS, need, stream=0,
+                                              check=False)
+        assert st == 0 and out == ns
 
 
 def st_of(name):

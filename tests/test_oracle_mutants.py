@@ -41,6 +41,13 @@ MUTANTS = [
     ("gather_shifted", "(const char*)src + (size_t)keep[j] * row_bytes",
      "(const char*)src + (size_t)(keep[j] > 0 ? keep[j] - 1 : 0) * row_bytes"),
     ("trigger_off_by_one", "if (*n_slots < B + p->buffer) return 0;", "if (*n_slots <= B + p->buffer) return 0;"),
+    ("holefill_mover_to_last_free", "const int dst = free_rows[m++];",
+     "const int dst = free_rows[free_rows.size() - 1 - m++];"),
+    ("holefill_stayer_moves", "new_order[j] = order[keep[j]];", "new_order[j] = keep[j];"),
+    ("holefill_v_not_moved", "std::memcpy((char*)v_rows + (size_t)dst * row_bytes",
+     "if (0) std::memcpy((char*)v_rows + (size_t)dst * row_bytes"),
+    ("holefill_padding_reuses_first_free", "for (int j = 0; j < lead; ++j) new_order[j] = free_rows[m + j];",
+     "for (int j = 0; j < lead; ++j) new_order[j] = free_rows[j];"),
 ]
 
 
