@@ -173,7 +173,7 @@ def cpu_baseline(cs, budget_s: float = 20.0):
             "ms_per_step": step_s * 1e3, "cpu_seconds": one * n}
 
 
-def kernel_table(w, ev_lens, moved, means):
+def kernel_table(w, ev_lens, moved, means, holefill=False):
     """Per-kernel algorithmic work per launch, achieved rates against the
     MI355X peaks, and the roofline entry of the dominant kernel. ev_lens: the
     valid lengths of the evicting sequences; moved: rows with keep[j] != j;
@@ -185,6 +185,8 @@ def kernel_table(w, ev_lens, moved, means):
     k3_bytes = per_seq_slices * sum(N * D * e + G * A * D * e + 12 * N for N in ev_lens)
     k4_bytes = per_seq_slices * sum(12 * N for N in ev_lens) + w.slices * w.budget * 4
     k5_bytes = 4 * D * e * moved
+    if holefill:  # plus each slice's keep list read and order table read and written
+        k5_bytes += w.slices * w.budget * 12
     mfma_peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_MFMA_PEAK_TFLOPS
     kernels = {
         "gram": {"us": means[0] * 1e3, "bound": "mfma", "flops": k3_flops, "bytes": k3_bytes,
@@ -197,9 +199,13 @@ def kernel_table(w, ev_lens, moved, means):
     for k in kernels.values():
         k["frac"] = k["achieved"] / k["peak"]
     dom = max(["gram", "compact"], key=lambda k: kernels[k]["us"])
+    if holefill:
+        kernels["compact"]["kernel"] = "holefill_kernel"
+        kernels["compact"]["bound"] = "latency"
     dk = kernels[dom]
     roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
-                "unit": dk["unit"], "frac": dk["frac"], "traffic": measured_traffic(dom, w.name)}
+                "unit": dk["unit"], "frac": dk["frac"],
+                "traffic": measured_traffic(dom, w.name) if not (holefill and dom == "compact") else None}
     return kernels, roofline
 
 
@@ -228,7 +234,8 @@ def sweep_main(args, w):
     cpu = None
     with torch.cuda.stream(stream):
         sw = synth.Sweep(w, seed=args.seed)
-        ds = synth.DeviceSweep(sw, device=dev)
+        holefill = args.layout == "holefill"
+        ds = synth.DeviceSweep(sw, device=dev, order=holefill)
         p = rkv.make_params(w.num_layers, w.batch, w.num_kv_heads, w.group, w.capacity, w.budget, w.buffer,
                             w.obs_window, w.beta, w.lam, w.tau, w.dtype)
         wsb = rkv.rkv_workspace_bytes(p)
@@ -249,15 +256,25 @@ def sweep_main(args, w):
             ev = hip.create(4)
             if r % 2 == 0:
                 hip.record(ev[0], sp)
-                st, ns = rkv.rkv_evict_step(p, ds.k_layers(), ds.v_layers(), ds.Q, ds.seq_start, ds.n_slots, ws,
-                                            wsb, stream=stream)
+                if holefill:
+                    st, ns = rkv.rkv_evict_step_holefill(p, ds.k_layers(), ds.v_layers(), ds.Q, ds.seq_start,
+                                                         ds.order, ds.n_slots, ws, wsb, stream=stream)
+                else:
+                    st, ns = rkv.rkv_evict_step(p, ds.k_layers(), ds.v_layers(), ds.Q, ds.seq_start, ds.n_slots,
+                                                ws, wsb, stream=stream)
                 hip.record(ev[1], sp)
+            elif holefill:
+                st, ns = rkv.rkv_evict_step_holefill_timed(p, ds.k_layers(), ds.v_layers(), ds.Q, ds.seq_start,
+                                                           ds.order, ds.n_slots, ws, wsb, ev, stream=stream)
             else:
                 st, ns = rkv.rkv_evict_step_timed(p, ds.k_layers(), ds.v_layers(), ds.Q, ds.seq_start, ds.n_slots,
                                                   ws, wsb, ev, stream=stream)
             assert ns == w.budget
             ds.n_slots = ns
-            mv = int((keep != ident[None, :]).sum().item())  # synchronises the stream
+            if holefill:
+                mv = int((keep >= w.budget).sum().item())  # synchronises the stream
+            else:
+                mv = int((keep != ident[None, :]).sum().item())  # synchronises the stream
             if r % 2 == 0:
                 plain.append((r, hip.elapsed_ms(ev[0], ev[1])))
             else:
@@ -273,7 +290,7 @@ def sweep_main(args, w):
     st_rounds = [x for x in staged if x[0] >= SWEEP_STEADY_FROM] or staged
     means = [percentile([x[1][i] for x in st_rounds], 50) for i in range(3)]
     mv_med = int(percentile([x[2] for x in st_rounds], 50))
-    kernels, roofline = kernel_table(w, [w.budget + w.buffer] * w.batch, mv_med, means)
+    kernels, roofline = kernel_table(w, [w.budget + w.buffer] * w.batch, mv_med, means, holefill=holefill)
     out = {
         "metric": METRIC,
         "value": 1000.0 / med,
@@ -295,7 +312,7 @@ def sweep_main(args, w):
                    "obs_window": w.obs_window, "beta": w.beta, "lambda": w.lam, "tau": w.tau,
                    "slices": w.slices, "n_slots": w.budget + w.buffer, "rounds": rounds,
                    "steady_state": f"median over rounds {SWEEP_STEADY_FROM}..{rounds - 1}, plain-step rounds",
-                   "llc_flush": True, "seed": args.seed},
+                   "llc_flush": True, "seed": args.seed, "layout": args.layout},
         "moved_rows_per_round": {"min": min(moved), "median": int(percentile(moved, 50)), "max": max(moved)},
         "wall_s": wall,
         "kernels": kernels,
@@ -359,6 +376,9 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="keep inputs warm in the last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rounds", type=int, default=0, help="sweep workloads: rounds to run (default: the recipe's)")
+    ap.add_argument("--layout", choices=["order-preserving", "holefill"], default="order-preserving",
+                    help="compaction layout: the order-preserving step (default) or the hole-filling one with "
+                         "its order sidecar")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -400,6 +420,10 @@ def main():
         flush_out = torch.zeros((), dtype=torch.int64, device=dev)
         k_layers = [K[l] for l in range(w.num_layers)]
         v_layers = [V[l] for l in range(w.num_layers)]
+        holefill = args.layout == "holefill"
+        if holefill:  # the identity order: the synthetic cache is laid out in age order
+            O0 = torch.arange(w.budget, dtype=torch.int32, device=dev).repeat(w.slices).contiguous()
+            O = O0.clone()
 
         # moved rows (keep[j] != j) of this input, for the compaction's algorithmic bytes
         n = cs.n_slots
@@ -410,7 +434,10 @@ def main():
         rkv.rkv_select(p, imp, red, S, n, keep, stream=stream)
         stream.synchronize()
         kp = keep.cpu().numpy().reshape(w.slices, w.budget)
-        moved = int(((kp >= 0) & (kp != np.arange(w.budget)[None, :])).sum())
+        if holefill:  # only kept tokens past the budget move
+            moved = int((kp >= w.budget).sum())
+        else:
+            moved = int(((kp >= 0) & (kp != np.arange(w.budget)[None, :])).sum())
         del imp, red, keep
 
         sp = stream.cuda_stream
@@ -420,19 +447,28 @@ def main():
             K.copy_(K0)
             V.copy_(V0)
             S.copy_(S0)
+            if holefill:
+                O.copy_(O0)
             if not args.no_flush:
                 torch.sum(flush.view(torch.int64), dim=(0,), out=flush_out)
 
         def plain_step(ev):
             prepare()
             hip.record(ev[0], sp)
-            st, ns = rkv.rkv_evict_step(p, k_layers, v_layers, Q, S, n, ws, wsb, stream=stream)
+            if holefill:
+                st, ns = rkv.rkv_evict_step_holefill(p, k_layers, v_layers, Q, S, O, n, ws, wsb, stream=stream)
+            else:
+                st, ns = rkv.rkv_evict_step(p, k_layers, v_layers, Q, S, n, ws, wsb, stream=stream)
             hip.record(ev[1], sp)
             assert ns == w.budget
 
         def staged_step(ev):
             prepare()
-            st, ns = rkv.rkv_evict_step_timed(p, k_layers, v_layers, Q, S, n, ws, wsb, ev, stream=stream)
+            if holefill:
+                st, ns = rkv.rkv_evict_step_holefill_timed(p, k_layers, v_layers, Q, S, O, n, ws, wsb, ev,
+                                                           stream=stream)
+            else:
+                st, ns = rkv.rkv_evict_step_timed(p, k_layers, v_layers, Q, S, n, ws, wsb, ev, stream=stream)
             assert ns == w.budget
 
         warm = hip.create(4)
@@ -463,7 +499,7 @@ def main():
     mean_ms = sum(step_ms) / len(step_ms)
 
     kernels, roofline = kernel_table(w, [int(cs.lengths[b]) for b in range(w.batch) if cs.lengths[b] > w.budget],
-                                     moved, [sum(x) / len(x) for x in stage_ms])
+                                     moved, [sum(x) / len(x) for x in stage_ms], holefill=holefill)
 
     out = {
         "metric": METRIC,
@@ -485,7 +521,8 @@ def main():
         "config": {"workload": w.name, "layers": w.num_layers, "batch": w.batch, "kv_heads": w.num_kv_heads,
                    "group": w.group, "head_dim": w.head_dim, "budget": w.budget, "buffer": w.buffer,
                    "obs_window": w.obs_window, "beta": w.beta, "lambda": w.lam, "tau": w.tau,
-                   "slices": w.slices, "n_slots": cs.n_slots, "llc_flush": not args.no_flush, "seed": args.seed},
+                   "slices": w.slices, "n_slots": cs.n_slots, "llc_flush": not args.no_flush, "seed": args.seed,
+                   "layout": args.layout},
         "wall_ms_per_iteration": wall * 1e3 / args.steps,
         "kernels": kernels,
         "roofline": roofline,

@@ -99,16 +99,27 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(Geom g, LayerP
 // and the free list as 16-bit slots and a bitmap of occupied slots.
 constexpr int kHoleThreads = 256;
 
-__device__ inline int block_sum_hole(int v, int* red) {
+// Exclusive prefix sum over the work-group (wave scans, one barrier pair);
+// *total receives the sum.
+__device__ inline int block_exscan_hole(int v, int* red, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  v = wave_sum_i(v);
-  if (lane == 0) red[w] = v;
-  __syncthreads();
-  int t = 0;
+  int x = v;
 #pragma unroll
-  for (int i = 0; i < kHoleThreads / 64; ++i) t += red[i];
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    x += lane >= o ? y : 0;
+  }
+  if (lane == 63) red[w] = x;
   __syncthreads();
-  return t;
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kHoleThreads / 64; ++i) {
+    before += i < w ? red[i] : 0;
+    all += red[i];
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
 }
 
 template <typename T>
@@ -126,7 +137,6 @@ __global__ __launch_bounds__(kHoleThreads) void holefill_kernel(Geom g, LayerPtr
   uint16_t* fl = ol + B;               // free physical slots, ascending
   uint32_t* used = (uint32_t*)(hole_lds + ((6 * (size_t)B + 15) & ~(size_t)15));
   __shared__ int red[kHoleThreads / 64];
-  __shared__ int scan[kHoleThreads];
 
   const int slice = xcd_remap(blockIdx.x, gridDim.x);
   int l, b, h;
@@ -145,8 +155,10 @@ __global__ __launch_bounds__(kHoleThreads) void holefill_kernel(Geom g, LayerPtr
     nstay += valid && kv < B ? 1 : 0;
   }
   for (int w = tid; w < nwords; w += kHoleThreads) used[w] = 0u;
-  nlead = block_sum_hole(nlead, red);  // new first valid virtual slot
-  nstay = block_sum_hole(nstay, red);  // kept tokens already below the budget
+  int both;  // the two counts in one reduction (each below 2^16)
+  block_exscan_hole((nlead << 16) | nstay, red, &both);
+  nlead = both >> 16;               // new first valid virtual slot
+  nstay = both & 0xFFFF;            // kept tokens already below the budget
   // 2. physical slots of the kept tokens that stay
   for (int j = tid; j < B; j += kHoleThreads) {
     const int kv = kl[j];
@@ -160,16 +172,8 @@ __global__ __launch_bounds__(kHoleThreads) void holefill_kernel(Geom g, LayerPtr
     const uint32_t valid = w == nwords - 1 && (B & 31) ? (1u << (B & 31)) - 1u : 0xFFFFFFFFu;
     cnt += __popc(~used[w] & valid);
   }
-  scan[tid] = cnt;
-  __syncthreads();
-  for (int off = 1; off < kHoleThreads; off <<= 1) {  // inclusive scan
-    const int add = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += add;
-    __syncthreads();
-  }
-  const int nfree = scan[kHoleThreads - 1];
-  int rank = scan[tid] - cnt;
+  int nfree;
+  int rank = block_exscan_hole(cnt, red, &nfree);
   for (int w = tid * per; w < min(nwords, (tid + 1) * per); ++w) {
     const uint32_t valid = w == nwords - 1 && (B & 31) ? (1u << (B & 31)) - 1u : 0xFFFFFFFFu;
     uint32_t f = ~used[w] & valid;
@@ -204,13 +208,26 @@ __global__ __launch_bounds__(kHoleThreads) void holefill_kernel(Geom g, LayerPtr
   const size_t sbase = ((size_t)b * g.H + h) * g.capacity * (size_t)RB;
   char* kb = (char*)k.p[l] + sbase;
   char* vb = (char*)v.p[l] + sbase;
-  for (int idx = tid; idx < 2 * nmov * U4_ROW; idx += kHoleThreads) {
-    const int kvsel = idx / (nmov * U4_ROW), rem = idx % (nmov * U4_ROW);
-    const int m = rem / U4_ROW, part = rem % U4_ROW;
-    const int src = kl[j0 + m];
-    if (m >= nfree || src == 0xFFFF || src < B) continue;
-    char* base = kvsel ? vb : kb;
-    store_nt(base + (size_t)fl[m] * RB + part * 16, load_nt(base + (size_t)src * RB + part * 16));
+  // (loads of a pass are all issued before its stores: no source is a destination)
+  constexpr int kPass = 16;  // 16-byte copies in flight per thread
+  const int ncopy = 2 * nmov * U4_ROW;
+  for (int i0 = 0; i0 < ncopy; i0 += kPass * kHoleThreads) {
+    u32x4n val[kPass];
+    char* dst[kPass];
+#pragma unroll
+    for (int u = 0; u < kPass; ++u) {
+      const int idx = i0 + u * kHoleThreads + tid;
+      const int kvsel = idx / (nmov * U4_ROW), rem = idx % (nmov * U4_ROW);
+      const int m = rem / U4_ROW, part = rem % U4_ROW;
+      const int src = idx < ncopy ? kl[j0 + m] : 0xFFFF;
+      const bool ok = idx < ncopy && m < nfree && src != 0xFFFF && src >= B;
+      char* base = kvsel ? vb : kb;
+      dst[u] = ok ? base + (size_t)fl[m] * RB + part * 16 : nullptr;
+      if (ok) val[u] = load_nt(base + (size_t)src * RB + part * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < kPass; ++u)
+      if (dst[u]) store_nt(dst[u], val[u]);
   }
   if (l == 0 && h == 0 && tid == 0) seq_start[b] = nlead;
 }

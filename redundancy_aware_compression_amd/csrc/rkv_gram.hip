@@ -93,6 +93,23 @@ __device__ inline void wait_later_blocks(int later) {
   }
 }
 
+// Waits until at most n of this wave's vector memory operations are
+// outstanding (n clamped to [0, 31], which only waits longer).
+__device__ inline void wait_vm(int n) {
+  switch (n < 0 ? 0 : (n < 31 ? n : 31)) {
+#define RKV_VM_CASE(i) \
+  case i:              \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(i)); break;
+    RKV_VM_CASE(0) RKV_VM_CASE(1) RKV_VM_CASE(2) RKV_VM_CASE(3) RKV_VM_CASE(4) RKV_VM_CASE(5) RKV_VM_CASE(6)
+    RKV_VM_CASE(7) RKV_VM_CASE(8) RKV_VM_CASE(9) RKV_VM_CASE(10) RKV_VM_CASE(11) RKV_VM_CASE(12)
+    RKV_VM_CASE(13) RKV_VM_CASE(14) RKV_VM_CASE(15) RKV_VM_CASE(16) RKV_VM_CASE(17) RKV_VM_CASE(18)
+    RKV_VM_CASE(19) RKV_VM_CASE(20) RKV_VM_CASE(21) RKV_VM_CASE(22) RKV_VM_CASE(23) RKV_VM_CASE(24)
+    RKV_VM_CASE(25) RKV_VM_CASE(26) RKV_VM_CASE(27) RKV_VM_CASE(28) RKV_VM_CASE(29) RKV_VM_CASE(30)
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(31)); break;
+#undef RKV_VM_CASE
+  }
+}
+
 // Issues this wave's share of the direct-to-LDS loads of one 64-row block:
 // row r of the block lands at st_rows + r*RB with 16-byte slot p holding the
 // row's bytes [16*(p ^ (r & 15)), +16). voff[q] is the lane's block-invariant
@@ -273,6 +290,8 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   __shared__ __align__(16) float rst_lds[RKV_MAX_QROWS * 2];   // per query row: max, 1 / sum of exp
   __shared__ __align__(16) float sv_lds[kHeadDim];             // sum of unit keys
   __shared__ __align__(16) char s_lds[32 * RB];                // s as MFMA rows; scratch before that
+  constexpr int KA = 4;  // GATHER: refills between an ORD load and its use
+  __shared__ __align__(16) int ord_lds[KA][kGramWaves][8];     // GATHER: order entries of a wave's 8 rows
   static_assert(kGramWaves * (2 * 16 * 2 + kHeadDim) * 4 <= 32 * RB, "merge scratch fits the s tile");
 
   const int slice = xcd_remap(blockIdx.x, gridDim.x);
@@ -312,65 +331,115 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   // ---- loads: the first row block, the queries (all waves), the rest of
   // the ring; the issue cursor walks the stream (block ibi of group ig)
   int ig = 0, ibi = 0;
-  // GATHER: physical slots of the wave's 8 rows of the cursor's block, read
-  // (scalar loads) one issue ahead; rows past the slice point past the buffer
-  // (eight named scalars: an array here ends up in scratch memory, whose
-  // accesses would count among the ring's vmcnt)
-  int on0 = 0, on1 = 0, on2 = 0, on3 = 0, on4 = 0, on5 = 0, on6 = 0, on7 = 0;
-  const int32_t* ord = GATHER ? order + (size_t)slice * g.budget : nullptr;
-  auto fetch_order = [&]() {
-    if constexpr (GATHER) {
-      const int vb = s0 + (ig * kGroupBlocks + ibi) * kRowBlock + 8 * wave;  // virtual slot of row 8 wave
-      auto phys_of = [&](int v) {
-        const int o = ord[min(v, g.budget - 1)];
-        return __builtin_amdgcn_readfirstlane(v < g.budget ? o : (v < g.n_slots ? v : g.n_slots));
-      };
-      on0 = phys_of(vb + 0);
-      on1 = phys_of(vb + 1);
-      on2 = phys_of(vb + 2);
-      on3 = phys_of(vb + 3);
-      on4 = phys_of(vb + 4);
-      on5 = phys_of(vb + 5);
-      on6 = phys_of(vb + 6);
-      on7 = phys_of(vb + 7);
-    }
-  };
-  // physical slot of the lane's row in load qq (row 8 wave + KPQ qq + lane / SLOTS)
-  auto lane_phys = [&](int qq) {
-    const int li = lane / S::SLOTS;
-    if constexpr (KPQ == 4) {
-      const int a = qq == 0 ? on0 : on4, b2 = qq == 0 ? on1 : on5, c = qq == 0 ? on2 : on6, d = qq == 0 ? on3 : on7;
-      return li == 0 ? a : li == 1 ? b2 : li == 2 ? c : d;
-    } else {
-      static_assert(KPQ == 2, "bf16 or fp32 rows");
-      const int a = qq == 0 ? on0 : qq == 1 ? on2 : qq == 2 ? on4 : on6;
-      const int b2 = qq == 0 ? on1 : qq == 1 ? on3 : qq == 2 ? on5 : on7;
-      return li == 0 ? a : b2;
-    }
-  };
-  auto issue_next = [&](int q) {  // stream block q (the cursor's block) into stage q % COUNT
-    const int rbase = (ig * kGroupBlocks + ibi) * kRowBlock;
-    if constexpr (GATHER) {
-      uint32_t off[S::PER];
-#pragma unroll
-      for (int qq = 0; qq < S::PER; ++qq) off[qq] = (uint32_t)lane_phys(qq) * RB + vpart[qq];
-      issue_rows<T>(ring + (q % S::COUNT) * S::BYTES, rk, off, 0u, wave);
-    } else {
-      issue_rows<T>(ring + (q % S::COUNT) * S::BYTES, rk, voff, (uint32_t)rbase * RB, wave);
-    }
+  auto cursor_step = [&]() {
     if (++ibi == nrb - ig * kGroupBlocks) {
       ++ig;
       ibi = 0;
     }
-    fetch_order();
   };
-  fetch_order();
-  issue_next(0);
-  issue_rows<T>(lds_addr(q_lds),
-                make_desc((const char*)obs_q + ((size_t)(l * g.batch + b) * g.H + h) * (size_t)g.qrows * RB,
-                          (uint32_t)g.qrows * RB),
-                voff, 0u, wave);
-  for (int q = 1; q < total && q < S::COUNT; ++q) issue_next(q);
+  const int pro_n = min(total, S::COUNT);  // blocks issued before the loop
+  // GATHER: the physical slots of a block's rows come from the order table.
+  // The prologue reads them with ordinary loads (for its blocks and for the
+  // first refill's), awaited before the first direct-to-LDS load. Later
+  // blocks' slots come through LDS: ORD(X), a direct-to-LDS load of the 8
+  // entries of each wave's rows, is issued two refills ahead, and read into
+  // registers (noff) at the end of the refill before X; ORD(X) is issued
+  // KA refills ahead, so that waiting for it needs no younger row block than
+  // the ring already waits for. Each wave's sequence of vector memory
+  // operations is therefore ORD(COUNT + 1) .. ORD(COUNT + KA - 1) (those
+  // before the stream's end), ROW(0), the queries, ROW(1) .. ROW(pro_n - 1),
+  // then per refill of block X: ORD(X + KA) (when X + KA < total) and ROW(X);
+  // end_row(X) counts the operations up to ROW(X), so every wait is exact.
+  const int o0 = GATHER ? max(0, min(KA - 1, total - S::COUNT - 1)) : 0;
+  auto end_row = [&](int X) -> int {
+    if (X == 0) return o0 + S::PER;
+    if (X < S::COUNT) return o0 + (X + 2) * S::PER;
+    const int nord = GATHER ? max(0, min(X, total - KA - 1) - S::COUNT + 1) : 0;
+    return o0 + (pro_n + 1) * S::PER + (X - S::COUNT + 1) * S::PER + nord;
+  };
+  // operations up to ORD(Y), Y > COUNT
+  auto end_ord = [&](int Y) -> int { return Y < S::COUNT + KA ? Y - S::COUNT : end_row(Y - KA) - S::PER; };
+  const int32_t* ord = GATHER ? order + (size_t)slice * g.budget : nullptr;
+  auto phys_of = [&](int v, int o) { return v < g.budget ? o : (v < g.n_slots ? v : g.n_slots); };
+  const u32x4_t odesc = GATHER ? make_desc(ord, (uint32_t)g.budget * 4u) : rk;
+  // virtual slot of row 0 of stream block X (uniform)
+  auto vbase_of = [&](int X) {
+    int gg = 0;
+    while (X >= nrb - gg * kGroupBlocks) X -= nrb - (gg++) * kGroupBlocks;
+    return s0 + (gg * kGroupBlocks + X) * kRowBlock;
+  };
+  // ORD(X): the order entries of the wave's 8 rows of block X (lanes 0..7)
+  auto issue_ord = [&](int X) {
+    if (lane < 8)
+      dma_to_lds4(odesc, lds_addr(&ord_lds[X % KA][wave][0]),
+                  (uint32_t)min(vbase_of(X) + 8 * wave + lane, g.budget - 1) * 4u, 0u);
+  };
+  auto issue_row = [&](int q, const uint32_t* off, int rbase) {
+    if constexpr (GATHER)
+      issue_rows<T>(ring + (q % S::COUNT) * S::BYTES, rk, off, 0u, wave);
+    else
+      issue_rows<T>(ring + (q % S::COUNT) * S::BYTES, rk, voff, (uint32_t)rbase * RB, wave);
+  };
+  uint32_t noff[S::PER];  // GATHER: the load offsets of the next refill's block
+  // a refill: block X = the cursor's block
+  auto issue_next = [&](int X) {
+    const int rbase = (ig * kGroupBlocks + ibi) * kRowBlock;
+    cursor_step();
+    if (GATHER && X + KA < total) issue_ord(X + KA);
+    issue_row(X, noff, rbase);
+    if (GATHER && X + 1 < total) {
+      wait_vm(end_row(X) - end_ord(X + 1));
+      asm volatile("" ::: "memory");  // the LDS reads below follow that wait
+      const int vb = s0 + (ig * kGroupBlocks + ibi) * kRowBlock + 8 * wave;
+#pragma unroll
+      for (int qq = 0; qq < S::PER; ++qq) {
+        const int kk = KPQ * qq + lane / S::SLOTS;
+        noff[qq] = (uint32_t)phys_of(vb + kk, ord_lds[(X + 1) % KA][wave][kk]) * RB + vpart[qq];
+      }
+    }
+  };
+  {
+    // the prologue's blocks and the first refill's
+    uint32_t poff[S::COUNT + 1][S::PER];
+    if constexpr (GATHER) {
+      int cg = 0, cb = 0;
+#pragma unroll
+      for (int X = 0; X <= S::COUNT; ++X) {
+#pragma unroll
+        for (int qq = 0; qq < S::PER; ++qq) {
+          const int v = s0 + (cg * kGroupBlocks + cb) * kRowBlock + 8 * wave + KPQ * qq + lane / S::SLOTS;
+          // (unconditional: a block past the stream gets an unused, in-range read)
+          poff[X][qq] = (uint32_t)phys_of(v, ord[min(v, g.budget - 1)]) * RB + vpart[qq];
+        }
+        if (++cb == nrb - cg * kGroupBlocks) {
+          ++cg;
+          cb = 0;
+        }
+      }
+      // all loads issued above; every value is awaited here, before any
+      // direct-to-LDS load
+#pragma unroll
+      for (int X = 0; X <= S::COUNT; ++X)
+#pragma unroll
+        for (int qq = 0; qq < S::PER; ++qq) asm volatile("" : "+v"(poff[X][qq]));
+#pragma unroll
+      for (int qq = 0; qq < S::PER; ++qq) noff[qq] = poff[S::COUNT][qq];
+      for (int Y = S::COUNT + 1; Y < S::COUNT + 1 + o0; ++Y) issue_ord(Y);
+    }
+    issue_row(0, poff[0], 0);
+    cursor_step();
+    issue_rows<T>(lds_addr(q_lds),
+                  make_desc((const char*)obs_q + ((size_t)(l * g.batch + b) * g.H + h) * (size_t)g.qrows * RB,
+                            (uint32_t)g.qrows * RB),
+                  voff, 0u, wave);
+#pragma unroll
+    for (int X = 1; X < S::COUNT; ++X) {
+      if (X < pro_n) {
+        issue_row(X, poff[X], (ig * kGroupBlocks + ibi) * kRowBlock);
+        cursor_step();
+      }
+    }
+  }
 
   const float scale = 1.0f / sqrtf((float)kHeadDim);
   const int alpha = g.alpha;
@@ -458,7 +527,8 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   using Later = std::integral_constant<bool, false>;
 
   // block 0 (and the queries) landed, then its norms and statistics
-  wait_later_blocks<S::PER>(min(total, S::COUNT) - 1);
+  // block 0 and the queries (issued after ROW(0), before ROW(1))
+  wait_vm(pro_n == 1 ? 0 : end_row(pro_n - 1) - 2 * S::PER - o0);
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -476,13 +546,15 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   // iteration from iteration 1 on (block q' - 1 + COUNT in iteration q'), the
   // last before this wait being max(COUNT - 1, q + COUNT - 2)
   auto advance = [&](int q) {
+    const int X = q - 1 + S::COUNT;  // the refill's block
+    const bool refill = q >= 1 && X < total;
     if (q + 1 < total) {
       const int last = min(total - 1, max(S::COUNT - 1, q + S::COUNT - 2));
-      wait_later_blocks<S::PER>(last - (q + 1));
+      wait_vm(end_row(last) - end_row(q + 1));
     }
     __syncthreads();  // block q's norms are in LDS, block q + 1 has landed, and
                       // every wave is done with block q - 1, whose stage is free
-    if (q >= 1 && q - 1 + S::COUNT < total) issue_next(q - 1 + S::COUNT);
+    if (refill) issue_next(X);
   };
 
   // Gram work of stream block q = block bi of group gg
