@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   __shared__ __align__(16) float sv_lds[kHeadDim];             // sum of unit keys
   __shared__ __align__(16) char s_lds[32 * RB];                // s as MFMA rows; scratch before that
   constexpr int KA = 4;  // GATHER: refills between an ORD load and its use
-  __shared__ __align__(16) int ord_lds[KA][kGramWaves][8];     // GATHER: order entries of a wave's 8 rows
+  __shared__ __align__(16) int ord_lds[GATHER ? KA : 1][kGramWaves][8];  // GATHER: order entries of a wave's rows
   static_assert(kGramWaves * (2 * 16 * 2 + kHeadDim) * 4 <= 32 * RB, "merge scratch fits the s tile");
 
   const int slice = xcd_remap(blockIdx.x, gridDim.x);
@@ -319,14 +319,15 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   // 16 (p ^ (r & 15)) .. of it (vpart)
   static_assert(S::PER * 64 / S::SLOTS * kGramWaves == kRowBlock, "each wave loads 8 whole rows");
   constexpr int KPQ = 64 / S::SLOTS;  // rows per load
-  uint32_t voff[S::PER], vpart[S::PER];
+  uint32_t voff[S::PER];
 #pragma unroll
   for (int q = 0; q < S::PER; ++q) {
     const int flat = (wave * S::PER + q) * 64 + lane;
     const int r = flat / S::SLOTS, p = flat % S::SLOTS;
-    vpart[q] = (uint32_t)(p ^ (r & 15)) * 16;
-    voff[q] = (uint32_t)r * RB + vpart[q];
+    voff[q] = (uint32_t)r * RB + (uint32_t)(p ^ (r & 15)) * 16;
   }
+  // the in-row part of load q's offset (row 8 wave + KPQ q + lane / SLOTS)
+  auto vpart = [&](int q) { return voff[q] - (uint32_t)(8 * wave + KPQ * q + lane / S::SLOTS) * RB; };
 
   // ---- loads: the first row block, the queries (all waves), the rest of
   // the ring; the issue cursor walks the stream (block ibi of group ig)
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
 #pragma unroll
       for (int qq = 0; qq < S::PER; ++qq) {
         const int kk = KPQ * qq + lane / S::SLOTS;
-        noff[qq] = (uint32_t)phys_of(vb + kk, ord_lds[(X + 1) % KA][wave][kk]) * RB + vpart[qq];
+        noff[qq] = (uint32_t)phys_of(vb + kk, ord_lds[(X + 1) % KA][wave][kk]) * RB + vpart(qq);
       }
     }
   };
@@ -409,7 +410,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
         for (int qq = 0; qq < S::PER; ++qq) {
           const int v = s0 + (cg * kGroupBlocks + cb) * kRowBlock + 8 * wave + KPQ * qq + lane / S::SLOTS;
           // (unconditional: a block past the stream gets an unused, in-range read)
-          poff[X][qq] = (uint32_t)phys_of(v, ord[min(v, g.budget - 1)]) * RB + vpart[qq];
+          poff[X][qq] = (uint32_t)phys_of(v, ord[min(v, g.budget - 1)]) * RB + vpart(qq);
         }
         if (++cb == nrb - cg * kGroupBlocks) {
           ++cg;
@@ -528,7 +529,10 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
 
   // block 0 (and the queries) landed, then its norms and statistics
   // block 0 and the queries (issued after ROW(0), before ROW(1))
-  wait_vm(pro_n == 1 ? 0 : end_row(pro_n - 1) - 2 * S::PER - o0);
+  if constexpr (GATHER)
+    wait_vm(pro_n == 1 ? 0 : end_row(pro_n - 1) - 2 * S::PER - o0);
+  else
+    wait_later_blocks<S::PER>(pro_n - 1);
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -550,7 +554,10 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
     const bool refill = q >= 1 && X < total;
     if (q + 1 < total) {
       const int last = min(total - 1, max(S::COUNT - 1, q + S::COUNT - 2));
-      wait_vm(end_row(last) - end_row(q + 1));
+      if constexpr (GATHER)
+        wait_vm(end_row(last) - end_row(q + 1));
+      else
+        wait_later_blocks<S::PER>(last - (q + 1));
     }
     __syncthreads();  // block q's norms are in LDS, block q + 1 has landed, and
                       // every wave is done with block q - 1, whose stage is free
