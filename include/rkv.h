@@ -229,6 +229,43 @@ rkv_status rkv_compact_holefill(const rkv_params* p, void* const* k_layers, void
                                 const int32_t* keep, int32_t* seq_start, int32_t* order, int32_t n_slots,
                                 void* stream);
 
+/*
+ * Sampled selection (ForesightKV explainer, technical summary: eviction is
+ * triggered at budget + L; the newest L tokens stay and the rest is
+ * compressed to budget - L from a scoring model's per-token importance, the
+ * eviction decision being a Top-K followed by multinomial sampling). The
+ * scores are the caller's (the learned scoring model is not part of this
+ * library). Per (layer, sequence, KV head) with N_b > budget: the newest
+ * keep_newest valid tokens are kept; of the other (candidate) tokens the
+ * top_k by score are retained first (equal scores: the later slot; top_k is
+ * raised to budget - keep_newest and capped at the candidate count), and
+ * budget - keep_newest of those are drawn without replacement with
+ * probabilities proportional to exp(score / temperature), in the
+ * Gumbel-top-k form: the largest score / temperature - log(-log u), u the
+ * caller's uniform for the slot. With N_b <= budget every valid token is
+ * kept.
+ *   scores, uniforms  float32 [num_layers][batch][num_kv_heads][n_slots],
+ *                     read at the valid slots; uniforms strictly in (0, 1)
+ *   keep_newest       L, 0 <= L < budget
+ *   top_k             >= 0; temperature > 0 and finite
+ *   keep              out, the layout of rkv_select's keep
+ * Errors as rkv_select, plus RKV_ERR_BAD_PARAM for keep_newest, top_k or
+ * temperature out of range.
+ */
+rkv_status rkv_select_sampled(const rkv_params* p, const float* scores, const float* uniforms,
+                              const int32_t* seq_start, int32_t n_slots, int32_t keep_newest, int32_t top_k,
+                              float temperature, int32_t* keep, void* stream);
+
+/* The eviction step with the sampled selection: the trigger of
+ * rkv_evict_step (n_slots >= budget + buffer, else a no-op), then
+ * rkv_select_sampled into the workspace's keep lists
+ * (rkv_workspace_keep_offset) and the order-preserving compaction of
+ * rkv_compact. *n_slots becomes budget. */
+rkv_status rkv_evict_step_sampled(const rkv_params* p, void* const* k_layers, void* const* v_layers,
+                                  const float* scores, const float* uniforms, int32_t* seq_start, int32_t* n_slots,
+                                  int32_t keep_newest, int32_t top_k, float temperature, void* ws, size_t ws_bytes,
+                                  void* stream);
+
 /* Static string naming a status. */
 const char* rkv_status_string(rkv_status st);
 

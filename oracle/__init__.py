@@ -72,6 +72,9 @@ def load_library(path: str):
     L.orc_gather_rows.restype = None
     L.orc_gather_rows.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_void_p]
+    L.orc_select_sampled.restype = ctypes.c_int32
+    L.orc_select_sampled.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     L.orc_holefill_slice.restype = ctypes.c_int32
     L.orc_holefill_slice.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
@@ -196,3 +199,17 @@ def holefill_slice(K: np.ndarray, V: np.ndarray, order: np.ndarray, keep: np.nda
     if lead < 0:
         raise ValueError("order is not a permutation of [0, budget) or keep is malformed")
     return K2, V2, o2, int(lead)
+
+
+def select_sampled(scores: np.ndarray, uniforms: np.ndarray, budget: int, keep_newest: int, top_k: int,
+                   temperature: float = 1.0) -> np.ndarray:
+    """orc_select_sampled on one slice: kept positions, ascending."""
+    sc = np.ascontiguousarray(scores, dtype=np.float32)
+    un = np.ascontiguousarray(uniforms, dtype=np.float32)
+    assert sc.shape == un.shape and sc.ndim == 1
+    out = np.empty(max(budget, sc.shape[0]), np.int32)
+    n = lib().orc_select_sampled(sc.shape[0], budget, keep_newest, top_k, temperature, sc.ctypes.data,
+                                 un.ctypes.data, out.ctypes.data)
+    if n < 0:
+        raise ValueError("invalid sampled-selection parameters")
+    return out[:n].copy()

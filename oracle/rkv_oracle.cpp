@@ -281,3 +281,36 @@ extern "C" int32_t orc_holefill_slice(void* k_rows, void* v_rows, int32_t row_by
   for (int v = 0; v < B; ++v) order[v] = new_order[v];
   return lead;
 }
+
+extern "C" int32_t orc_select_sampled(int32_t n, int32_t budget, int32_t keep_newest, int32_t top_k,
+                                      double temperature, const float* scores, const float* uniforms,
+                                      int32_t* keep_out) {
+  /* [FKV] ForesightKV explainer, technical summary: keep the newest L
+   * tokens, compress the rest to B - L; Top-K, then multinomial sampling. */
+  if (n < 0 || budget < 1 || keep_newest < 0 || keep_newest >= budget || top_k < 0 || !(temperature > 0.0))
+    return -1;
+  if (n <= budget) {
+    for (int j = 0; j < n; ++j) keep_out[j] = j;
+    return n;
+  }
+  const int nc = n - keep_newest, kk = budget - keep_newest;
+  const int K = std::min(std::max(top_k, kk), nc);
+  // the top K candidates by score, equal scores to the later position
+  std::vector<int> cand(nc);
+  for (int i = 0; i < nc; ++i) cand[i] = i;
+  std::sort(cand.begin(), cand.end(), [&](int a, int b) {
+    const double sa = scores[a], sb = scores[b];
+    return sa != sb ? sa > sb : a > b;
+  });
+  cand.resize(K);
+  // a draw of kk without replacement, probabilities proportional to
+  // exp(score / T): the kk largest Gumbel-perturbed keys
+  std::vector<double> key(nc, 0.0);
+  for (int i : cand) key[i] = (double)scores[i] / temperature - std::log(-std::log((double)uniforms[i]));
+  std::sort(cand.begin(), cand.end(), [&](int a, int b) { return key[a] != key[b] ? key[a] > key[b] : a > b; });
+  std::vector<int> kept(cand.begin(), cand.begin() + kk);
+  for (int j = nc; j < n; ++j) kept.push_back(j);
+  std::sort(kept.begin(), kept.end());
+  for (int j = 0; j < budget; ++j) keep_out[j] = kept[j];
+  return budget;
+}

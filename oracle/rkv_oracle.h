@@ -103,6 +103,21 @@ void orc_gather_rows(const void* src, const int32_t* keep, int32_t n_keep, int32
 int32_t orc_holefill_slice(void* k_rows, void* v_rows, int32_t row_bytes, int32_t budget, int32_t n_slots,
                            const int32_t* keep, int32_t* order);
 
+/*
+ * Sampled selection of one slice with n valid tokens (positions 0..n-1):
+ * ForesightKV's Top-K followed by multinomial sampling on caller scores. The
+ * newest keep_newest tokens are kept; among the others the K = min(max(top_k,
+ * budget - keep_newest), candidates) best by score (equal scores: the later
+ * position) survive, and budget - keep_newest of the survivors are drawn
+ * without replacement with probabilities proportional to
+ * exp(score / temperature): the largest score / temperature - log(-log u)
+ * (the Gumbel-top-k form of that draw; u in (0, 1) per token, equal keys:
+ * the later position). With n <= budget all are kept. keep_out receives the
+ * kept positions ascending; returns their count, or -1 on invalid input.
+ */
+int32_t orc_select_sampled(int32_t n, int32_t budget, int32_t keep_newest, int32_t top_k, double temperature,
+                           const float* scores, const float* uniforms, int32_t* keep_out);
+
 #ifdef __cplusplus
 }
 #endif

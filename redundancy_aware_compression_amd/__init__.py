@@ -26,10 +26,12 @@ from ._binding import (  # noqa: F401
     rkv_evict_step,
     rkv_evict_step_holefill,
     rkv_evict_step_holefill_timed,
+    rkv_evict_step_sampled,
     rkv_evict_step_timed,
     rkv_last_hip_error,
     rkv_score,
     rkv_select,
+    rkv_select_sampled,
     rkv_status_string,
     rkv_workspace_bytes,
     rkv_workspace_keep_offset,

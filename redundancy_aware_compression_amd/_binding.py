@@ -96,6 +96,11 @@ def _lib():
         L.rkv_evict_step_holefill_timed.argtypes = [P, vp, vp, vp, vp, vp, ctypes.POINTER(i32), vp, sz, vp, vp]
         L.rkv_compact_holefill.restype = ctypes.c_int
         L.rkv_compact_holefill.argtypes = [P, vp, vp, vp, vp, vp, i32, vp]
+        f32 = ctypes.c_float
+        L.rkv_select_sampled.restype = ctypes.c_int
+        L.rkv_select_sampled.argtypes = [P, vp, vp, vp, i32, i32, i32, f32, vp, vp]
+        L.rkv_evict_step_sampled.restype = ctypes.c_int
+        L.rkv_evict_step_sampled.argtypes = [P, vp, vp, vp, vp, vp, ctypes.POINTER(i32), i32, i32, f32, vp, sz, vp]
         L.rkv_status_string.restype = ctypes.c_char_p
         L.rkv_status_string.argtypes = [ctypes.c_int]
         L.rkv_last_hip_error.restype = ctypes.c_int
@@ -239,3 +244,24 @@ def rkv_compact_holefill(p: RkvParams, k_layers: Sequence, v_layers: Sequence, k
                                      ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(keep),
                                      _ptr(seq_start), _ptr(order), n_slots, _stream(stream))
     return _check(st, "rkv_compact_holefill") if check else st
+
+
+def rkv_select_sampled(p: RkvParams, scores, uniforms, seq_start, n_slots: int, keep_newest: int, top_k: int,
+                       temperature: float, keep, stream=None, check: bool = True) -> int:
+    st = _lib().rkv_select_sampled(ctypes.byref(p), _ptr(scores), _ptr(uniforms), _ptr(seq_start), n_slots,
+                                   keep_newest, top_k, temperature, _ptr(keep), _stream(stream))
+    return _check(st, "rkv_select_sampled") if check else st
+
+
+def rkv_evict_step_sampled(p: RkvParams, k_layers: Sequence, v_layers: Sequence, scores, uniforms, seq_start,
+                           n_slots: int, keep_newest: int, top_k: int, temperature: float, ws, ws_bytes: int,
+                           stream=None, check: bool = True):
+    """The eviction step with the sampled selection; returns (status, n_slots after the step)."""
+    ns = ctypes.c_int32(n_slots)
+    st = _lib().rkv_evict_step_sampled(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
+                                       ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(scores),
+                                       _ptr(uniforms), _ptr(seq_start), ctypes.byref(ns), keep_newest, top_k,
+                                       temperature, _ptr(ws), ws_bytes, _stream(stream))
+    if check:
+        _check(st, "rkv_evict_step_sampled")
+    return st, ns.value

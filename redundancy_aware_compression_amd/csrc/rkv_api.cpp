@@ -2,6 +2,7 @@
 // Validation runs entirely on the host before anything is enqueued, so every
 // error path leaves device memory untouched and needs no GPU.
 #include <hip/hip_runtime_api.h>
+#include <math.h>
 #include <string.h>
 
 #include "rkv.h"
@@ -242,6 +243,55 @@ rkv_status rkv_compact_holefill(const rkv_params* p, void* const* k_layers, void
   const rkv::Geom g = make_geom(p, n_slots);
   RKV_TRY(rkv::launch_compact_holefill(g, p->dtype, make_layers(p, (const void* const*)k_layers),
                                        make_layers(p, (const void* const*)v_layers), keep, order, seq_start, stream));
+  return RKV_OK;
+}
+
+namespace {
+
+rkv_status check_sampled(const rkv_params* p, int32_t keep_newest, int32_t top_k, float temperature) {
+  if (keep_newest < 0 || keep_newest >= p->budget) return RKV_ERR_BAD_PARAM;
+  if (top_k < 0) return RKV_ERR_BAD_PARAM;
+  if (!(temperature > 0.f) || !(temperature < INFINITY)) return RKV_ERR_BAD_PARAM;
+  return RKV_OK;
+}
+
+}  // namespace
+
+rkv_status rkv_select_sampled(const rkv_params* p, const float* scores, const float* uniforms,
+                              const int32_t* seq_start, int32_t n_slots, int32_t keep_newest, int32_t top_k,
+                              float temperature, int32_t* keep, void* stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  if ((st = check_sampled(p, keep_newest, top_k, temperature)) != RKV_OK) return st;
+  if (!scores || !uniforms || !seq_start || !keep) return RKV_ERR_NULL_ARG;
+  if (n_slots < p->budget || n_slots > p->capacity) return RKV_ERR_BAD_SHAPE;
+  const rkv::Geom g = make_geom(p, n_slots);
+  RKV_TRY(rkv::launch_select_sampled(g, scores, uniforms, seq_start, keep_newest, top_k, temperature, keep, stream));
+  return RKV_OK;
+}
+
+rkv_status rkv_evict_step_sampled(const rkv_params* p, void* const* k_layers, void* const* v_layers,
+                                  const float* scores, const float* uniforms, int32_t* seq_start, int32_t* n_slots,
+                                  int32_t keep_newest, int32_t top_k, float temperature, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  if ((st = check_sampled(p, keep_newest, top_k, temperature)) != RKV_OK) return st;
+  if ((st = check_layers(p, (const void* const*)k_layers)) != RKV_OK) return st;
+  if ((st = check_layers(p, (const void* const*)v_layers)) != RKV_OK) return st;
+  if (!scores || !uniforms || !seq_start || !n_slots || !ws) return RKV_ERR_NULL_ARG;
+  if ((uintptr_t)ws & 255u) return RKV_ERR_MISALIGNED;
+  const int32_t ns = *n_slots;
+  if (ns < 0 || ns > p->capacity) return RKV_ERR_BAD_SHAPE;
+  rkv::Workspace w = rkv::carve(*p, ws);
+  if (ws_bytes < w.bytes) return RKV_ERR_WORKSPACE_TOO_SMALL;
+  if (ns < p->budget + p->buffer) return RKV_OK;  // below the trigger: no-op
+  const rkv::Geom g = make_geom(p, ns);
+  RKV_TRY(rkv::launch_select_sampled(g, scores, uniforms, seq_start, keep_newest, top_k, temperature, w.keep,
+                                     stream));
+  RKV_TRY(rkv::launch_compact(g, p->dtype, make_layers(p, (const void* const*)k_layers),
+                              make_layers(p, (const void* const*)v_layers), w.keep, seq_start, stream));
+  *n_slots = p->budget;
   return RKV_OK;
 }
 

@@ -76,6 +76,8 @@ int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q,
                 const int32_t* order, float* importance, float* rowmean, int32_t* counts, void* stream);
 int launch_redundancy(const Geom& g, const int32_t* seq_start, const int32_t* counts, const float* rowmean,
                       float* redundancy, void* stream);
+int launch_select_sampled(const Geom& g, const float* scores, const float* uniforms, const int32_t* seq_start,
+                          int keep_newest, int top_k, float temperature, int32_t* keep, void* stream);
 int launch_select(const Geom& g, const float* importance, const float* redundancy, const int32_t* counts,
                   const float* rowmean, const int32_t* seq_start, int32_t* keep, float* z_out, float* r_out,
                   void* stream);

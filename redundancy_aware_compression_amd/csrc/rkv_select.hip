@@ -27,6 +27,61 @@ __device__ inline uint32_t order_key(float z) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Exact k-th largest of keys[0 .. n) (1 <= k <= n) by four 8-bit radix
+// passes over an LDS histogram: T is that key and `need` the number of keys
+// equal to T among the top k. Every thread of the work-group takes part and
+// receives both.
+__device__ inline void radix_kth(const uint32_t* keys, int n, int k, int* hist, int* sel_digit, int* sel_above,
+                                 uint32_t& T, int& need) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  uint32_t prefix = 0;
+  need = k;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    for (int d = tid; d < 256; d += nt) hist[d] = 0;
+    if (tid == 0) {
+      *sel_digit = 0;
+      *sel_above = 0;
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += nt) {
+      const uint32_t key = keys[i];
+      if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l owns digits 4l..4l+3; suffix sums from the top digit down
+      const int c0 = hist[4 * tid], c1 = hist[4 * tid + 1], c2 = hist[4 * tid + 2], c3 = hist[4 * tid + 3];
+      const int own = c0 + c1 + c2 + c3;
+      int incl = own;  // sum over lanes >= tid
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_down(incl, o);
+        if (tid + o < 64) incl += y;
+      }
+      const int above_lane = incl - own;  // keys in digits above 4*tid+3
+      // the digit d with above(d) < need <= above(d) + hist[d] lies in exactly one lane
+      int a3 = above_lane, a2 = a3 + c3, a1 = a2 + c2, a0 = a1 + c1;
+      int d = -1, ab = 0;
+      if (a3 < need && need <= a3 + c3) { d = 4 * tid + 3; ab = a3; }
+      else if (a2 < need && need <= a2 + c2) { d = 4 * tid + 2; ab = a2; }
+      else if (a1 < need && need <= a1 + c1) { d = 4 * tid + 1; ab = a1; }
+      else if (a0 < need && need <= a0 + c0) { d = 4 * tid; ab = a0; }
+      if (d >= 0) {
+        *sel_digit = d;
+        *sel_above = ab;
+      }
+    }
+    __syncthreads();
+    need -= *sel_above;
+    prefix |= (uint32_t)*sel_digit << shift;
+    __syncthreads();
+  }
+  T = prefix;
+}
+
 // FROM_COUNTS: redundancy = counts < beta ? 0 : rowmean (the eviction step);
 // otherwise read the given redundancy array (the standalone select call).
 template <bool FROM_COUNTS>
@@ -89,52 +144,9 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Geom g, const fl
   __syncthreads();
 
   // ---- radix select: exact k-th largest key T, and how many keys equal to T to take
-  uint32_t prefix = 0;
-  int need = kk;
-#pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for (int d = tid; d < 256; d += nt) hist[d] = 0;
-    if (tid == 0) {
-      sel_digit = 0;
-      sel_above = 0;
-    }
-    __syncthreads();
-    for (int i = tid; i < nc; i += nt) {
-      const uint32_t key = keys[i];
-      if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      // lane l owns digits 4l..4l+3; suffix sums from the top digit down
-      const int c0 = hist[4 * tid], c1 = hist[4 * tid + 1], c2 = hist[4 * tid + 2], c3 = hist[4 * tid + 3];
-      const int own = c0 + c1 + c2 + c3;
-      int incl = own;  // sum over lanes >= tid
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_down(incl, o);
-        if (tid + o < 64) incl += y;
-      }
-      const int above_lane = incl - own;  // keys in digits above 4*tid+3
-      // the digit d with above(d) < need <= above(d) + hist[d] lies in exactly one lane
-      int a3 = above_lane, a2 = a3 + c3, a1 = a2 + c2, a0 = a1 + c1;
-      int d = -1, ab = 0;
-      if (a3 < need && need <= a3 + c3) { d = 4 * tid + 3; ab = a3; }
-      else if (a2 < need && need <= a2 + c2) { d = 4 * tid + 2; ab = a2; }
-      else if (a1 < need && need <= a1 + c1) { d = 4 * tid + 1; ab = a1; }
-      else if (a0 < need && need <= a0 + c0) { d = 4 * tid; ab = a0; }
-      if (d >= 0) {
-        sel_digit = d;
-        sel_above = ab;
-      }
-    }
-    __syncthreads();
-    need -= sel_above;
-    prefix |= (uint32_t)sel_digit << shift;
-    __syncthreads();
-  }
-  const uint32_t T = prefix;
+  uint32_t T;
+  int need;
+  radix_kth(keys, nc, kk, hist, &sel_digit, &sel_above, T, need);
 
   // ---- keys equal to T: keep the `need` latest ones. Each thread owns a
   // contiguous range of candidates; a suffix count over threads gives every
@@ -181,6 +193,116 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Geom g, const fl
       if (sel && --pos < B) krow[pos] = s0 + i;  // pos < B always; the guard only bounds the write
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Sampled selection (ForesightKV page, technical summary: when the cache
+// reaches budget + L, the newest L tokens stay and the rest is compressed to
+// budget - L by a Top-K followed by multinomial sampling on the scores of a
+// learned scoring model; the scores are the caller's). Per slice, among the
+// candidates (every valid token but the newest keep_newest): the top_k by
+// score (equal scores: the later slot), then budget - keep_newest of those
+// drawn without replacement with probabilities proportional to
+// exp(score / temperature). The draw is the Gumbel-top-k form of that
+// sampling: the largest score / temperature - log(-log u) among the top_k,
+// u the caller's uniform in (0, 1) for the slot (the same law as drawing one
+// token at a time, each with probability proportional to exp(score / T)
+// among those left).
+__global__ __launch_bounds__(kSelectThreads) void select_sampled_kernel(Geom g, const float* __restrict__ scores,
+                                                                        const float* __restrict__ uniforms,
+                                                                        const int32_t* __restrict__ seq_start,
+                                                                        int keep_newest, int top_k, float inv_temp,
+                                                                        int32_t* __restrict__ keep) {
+  __shared__ uint32_t keys[RKV_MAX_CAPACITY];
+  __shared__ int hist[256];
+  __shared__ int iscr[16];
+  __shared__ int sel_digit, sel_above;
+
+  const int slice = blockIdx.x;
+  int l, b, h, s0, N;
+  slice_coords(g, slice, l, b, h);
+  seq_range(g, seq_start, b, s0, N);
+  const int tid = threadIdx.x, nt = blockDim.x;
+  int32_t* krow = keep + (size_t)slice * g.budget;
+  const int B = g.budget;
+  if (N <= B) {  // keep every valid token, right-aligned
+    for (int j = tid; j < B; j += nt) krow[j] = j >= B - N ? j + (g.n_slots - B) : -1;
+    return;
+  }
+  const int nc = N - keep_newest, kk = B - keep_newest;
+  const int K = min(max(top_k, kk), nc);
+  const size_t base = (size_t)slice * g.n_slots + s0;
+  for (int i = tid; i < nc; i += nt) keys[i] = order_key(scores[base + i]);
+  __syncthreads();
+  // each thread owns a contiguous range of the valid tokens
+  const int seg = (N + nt - 1) / nt;
+  const int lo = tid * seg, hi = min(N, lo + seg);
+  // 1. the top K by score; survivors get their Gumbel key, the rest key 0
+  //    (below every float's key)
+  {
+    uint32_t T;
+    int need;
+    radix_kth(keys, nc, K, hist, &sel_digit, &sel_above, T, need);
+    int eq_here = 0;
+    for (int i = lo; i < hi && i < nc; ++i) eq_here += keys[i] == T;
+    int eq_total;
+    const int eq_before = block_exclusive_scan(eq_here, iscr, &eq_total);
+    int ea = eq_total - eq_before - eq_here;
+    for (int i = min(hi, nc) - 1; i >= lo; --i) {
+      const uint32_t key = keys[i];
+      const bool sel = key > T || (key == T && ea < need);
+      if (key == T) ++ea;
+      const float u = uniforms[base + i];
+      keys[i] = sel ? order_key(scores[base + i] * inv_temp - logf(-logf(u))) : 0u;
+    }
+    __syncthreads();
+  }
+  // 2. the top kk of the Gumbel keys, then the kept slots in ascending order
+  uint32_t T;
+  int need;
+  radix_kth(keys, nc, kk, hist, &sel_digit, &sel_above, T, need);
+  int eq_here = 0;
+  for (int i = lo; i < hi && i < nc; ++i) eq_here += keys[i] == T;
+  int eq_total;
+  const int eq_before = block_exclusive_scan(eq_here, iscr, &eq_total);
+  const int eq_after = eq_total - eq_before - eq_here;
+  int kept_here = 0;
+  {
+    int ea = eq_after;
+    for (int i = hi - 1; i >= lo; --i) {
+      bool sel = true;  // the newest keep_newest tokens
+      if (i < nc) {
+        const uint32_t key = keys[i];
+        sel = key > T || (key == T && ea < need);
+        if (key == T) ++ea;
+      }
+      kept_here += sel;
+    }
+  }
+  int kept_total;
+  const int out = block_exclusive_scan(kept_here, iscr, &kept_total);
+  {
+    int ea = eq_after;
+    int pos = out + kept_here;
+    for (int i = hi - 1; i >= lo; --i) {
+      bool sel = true;
+      if (i < nc) {
+        const uint32_t key = keys[i];
+        sel = key > T || (key == T && ea < need);
+        if (key == T) ++ea;
+      }
+      if (sel && --pos < B) krow[pos] = s0 + i;
+    }
+  }
+}
+
+int launch_select_sampled(const Geom& g, const float* scores, const float* uniforms, const int32_t* seq_start,
+                          int keep_newest, int top_k, float temperature, int32_t* keep, void* stream) {
+  const int slices = g.L * g.batch * g.H;
+  if (slices == 0) return 0;
+  hipLaunchKernelGGL(select_sampled_kernel, dim3(slices), dim3(kSelectThreads), 0, (hipStream_t)stream, g, scores,
+                     uniforms, seq_start, keep_newest, top_k, 1.f / temperature, keep);
+  return (int)hipGetLastError();
 }
 
 int launch_select(const Geom& g, const float* importance, const float* redundancy, const int32_t* counts,

@@ -32,7 +32,7 @@ BF16 = 0
 F32 = 1
 
 # tensor ids of the per-slice streams
-T_KEYS, T_VALUES, T_QUERIES, T_LENGTHS, T_MIX = 0, 1, 2, 3, 4
+T_KEYS, T_VALUES, T_QUERIES, T_LENGTHS, T_MIX, T_SCORES, T_UNIFORMS = 0, 1, 2, 3, 4, 5, 6
 
 BF16_NAN = 0x7FC0
 BF16_CANARY = 0x7F81  # a signalling-NaN pattern no generator or copy produces
@@ -74,6 +74,8 @@ def lib():
         L.synth_repeat_plan.argtypes = [u64, i32, i32, dbl, i32, vp]
         L.synth_repeat_apply.restype = None
         L.synth_repeat_apply.argtypes = [u64, i32, i32, i32, vp, dbl, vp, i32, vp]
+        L.synth_fill_uniform_open.restype = None
+        L.synth_fill_uniform_open.argtypes = [u64, vp, i64]
         L.synth_bf16_from_f32.restype = ctypes.c_uint16
         L.synth_bf16_from_f32.argtypes = [ctypes.c_float]
         _lib = L
@@ -519,3 +521,21 @@ class DeviceSweep:
         self.seq_start.zero_()
         self.n_slots = B + n
         return rnd
+
+
+
+def sampled_inputs(w: Workload, seed: int = 0):
+    """Per-slot scores (N(0, 1), float32) and uniforms (strictly inside (0, 1),
+    float32) of every slice, [L][b][H][n_slots]: the caller-side inputs of the
+    sampled selection (a learned scorer's outputs and the draw's randomness)."""
+    L = lib()
+    shape = (w.num_layers, w.batch, w.num_kv_heads, w.n_slots)
+    sc = np.empty(shape, np.float32)
+    un = np.empty(shape, np.float32)
+    for l in range(w.num_layers):
+        for b in range(w.batch):
+            for h in range(w.num_kv_heads):
+                L.synth_fill_normal(stream_key(seed, w.wid, T_SCORES, l, b, h), 0.0, 1.0, F32, _ptr(sc[l, b, h]),
+                                    w.n_slots)
+                L.synth_fill_uniform_open(stream_key(seed, w.wid, T_UNIFORMS, l, b, h), _ptr(un[l, b, h]), w.n_slots)
+    return sc, un

@@ -246,3 +246,10 @@ void synth_repeat_apply(uint64_t key, int32_t n_new, int32_t d, int32_t block_le
     ++w;
   }
 }
+
+/* out[i] = a float32 uniform strictly inside (0, 1): (24 random bits + 1/2)
+ * / 2^24, exact in float32, for i < n. */
+void synth_fill_uniform_open(uint64_t key, float* out, int64_t n) {
+  synth_stream s = {key, 0, 0.0};
+  for (int64_t i = 0; i < n; ++i) out[i] = (float)(((double)(sm64_next(&s) >> 40) + 0.5) * (1.0 / 16777216.0));
+}

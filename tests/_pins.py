@@ -377,6 +377,97 @@ def check_holefill_rejects_bad_order():
         raise AssertionError(f"accepted {bad}")
 
 
+def _uniforms(rng, n):
+    """Uniforms strictly inside (0, 1), exact in float32."""
+    return ((rng.integers(0, 1 << 24, size=n) + 0.5) / float(1 << 24)).astype(np.float32)
+
+
+def check_sampled_top_k_is_deterministic():
+    """With top_k = budget - keep_newest the draw has nothing to choose: the
+    kept set is the plain top of the scores (equal scores: the later
+    position) plus the newest tokens, whatever the uniforms."""
+    rng = np.random.default_rng(21)
+    for _ in range(100):
+        n = int(rng.integers(5, 40))
+        B = int(rng.integers(2, n))
+        L = int(rng.integers(0, B))
+        sc = rng.integers(-3, 4, size=n).astype(np.float32)  # many equal scores
+        got = oracle.select_sampled(sc, _uniforms(rng, n), B, L, B - L)
+        cand = sorted(range(n - L), key=lambda i: (-float(sc[i]), -i))[:B - L]
+        assert got.tolist() == sorted(cand + list(range(n - L, n))), (n, B, L)
+
+
+def check_sampled_equal_scores():
+    """Equal scores and no Top-K restriction: exp(score / T) is the same for
+    every candidate and -log(-log u) is increasing in u, so the draw keeps
+    the candidates with the largest uniforms."""
+    rng = np.random.default_rng(22)
+    for _ in range(50):
+        n = int(rng.integers(5, 60))
+        B = int(rng.integers(2, n))
+        L = int(rng.integers(0, B))
+        u = _uniforms(rng, n)
+        got = oracle.select_sampled(np.full(n, 0.3, np.float32), u, B, L, n, temperature=0.5)
+        cand = sorted(range(n - L), key=lambda i: -float(u[i]))[:B - L]
+        assert got.tolist() == sorted(cand + list(range(n - L, n)))
+
+
+def _inclusion_exact(w, m):
+    """Probability that each item is among m drawn without replacement, each
+    draw proportional to w among those left (enumerating ordered draws)."""
+    import itertools
+    K = len(w)
+    inc = np.zeros(K)
+    for seq in itertools.permutations(range(K), m):
+        pr, left = 1.0, float(sum(w))
+        for i in seq:
+            pr *= w[i] / left
+            left -= w[i]
+        for i in seq:
+            inc[i] += pr
+    return inc
+
+
+def check_sampled_inclusion_probabilities():
+    """The draw's law: over many seeded uniform vectors, how often each
+    candidate is kept matches the exact inclusion probability of drawing
+    budget - keep_newest items one at a time with probability proportional to
+    exp(score / T) among the top_k left (within 4.5 standard errors); items
+    outside the top_k are never kept."""
+    rng = np.random.default_rng(23)
+    sc = np.array([0.0, 0.5, 1.0, 1.5, -1.0, 0.25, 2.0], np.float32)
+    n, L, T, D = len(sc), 1, 0.7, 40000
+    for top_k, B in ((6, 3), (4, 3), (6, 4)):
+        nc, m = n - L, B - L
+        order = sorted(range(nc), key=lambda i: (-float(sc[i]), -i))[:top_k]
+        p = np.zeros(nc)
+        p[order] = _inclusion_exact([np.exp(float(sc[i]) / T) for i in order], m)
+        cnt = np.zeros(nc)
+        for _ in range(D):
+            kept = oracle.select_sampled(sc, _uniforms(rng, n), B, L, top_k, temperature=T)
+            assert kept[-1] == n - 1 and len(kept) == B
+            cnt[kept[:-1]] += 1
+        f = cnt / D
+        tol = 4.5 * np.sqrt(p * (1 - p) / D) + 1e-9
+        assert np.all(np.abs(f - p) <= tol), (top_k, B, f.round(4).tolist(), p.round(4).tolist())
+
+
+def check_sampled_scale_invariance():
+    """Scores and temperature scaled by the same power of two keep the same
+    set (score / T is unchanged exactly)."""
+    rng = np.random.default_rng(24)
+    for _ in range(30):
+        n = int(rng.integers(8, 50))
+        B = int(rng.integers(3, n))
+        L = int(rng.integers(0, B))
+        sc = rng.standard_normal(n).astype(np.float32)
+        u = _uniforms(rng, n)
+        k = int(rng.integers(B - L, n))
+        a = oracle.select_sampled(sc, u, B, L, k, temperature=0.8)
+        b = oracle.select_sampled(sc * np.float32(4), u, B, L, k, temperature=3.2)
+        assert np.array_equal(a, b)
+
+
 ALL_CHECKS = [
     check_hand_cases,
     check_lambda1_textbook,
@@ -393,4 +484,8 @@ ALL_CHECKS = [
     check_holefill_hand_cases,
     check_holefill_invariants,
     check_holefill_rejects_bad_order,
+    check_sampled_top_k_is_deterministic,
+    check_sampled_equal_scores,
+    check_sampled_inclusion_probabilities,
+    check_sampled_scale_invariance,
 ]

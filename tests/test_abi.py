@@ -116,6 +116,28 @@ def test_bad_params_rejected_by_every_entry_point(kw, expect):
     assert rkv.rkv_compact_holefill(p, layers(), layers(), FAKE, FAKE, FAKE, 300, stream=0, check=False) == code
 
 
+def test_sampled_argument_errors():
+    """The sampled selection: keep_newest, top_k and temperature ranges, NULL
+    inputs, and the step's no-op below the trigger."""
+    p = P()
+    need = rkv.rkv_workspace_bytes(p)
+    BADP, NULL = st_of("RKV_ERR_BAD_PARAM"), st_of("RKV_ERR_NULL_ARG")
+    for kn, tk, temp in ((-1, 10, 1.0), (256, 10, 1.0), (8, -1, 1.0), (8, 10, 0.0), (8, 10, float("inf")),
+                         (8, 10, float("nan"))):
+        assert rkv.rkv_select_sampled(p, FAKE, FAKE, FAKE, 300, kn, tk, temp, FAKE, stream=0, check=False) == BADP
+        st, _ = rkv.rkv_evict_step_sampled(p, layers(), layers(), FAKE, FAKE, FAKE, 384, kn, tk, temp, FAKE_WS, need,
+                                           stream=0, check=False)
+        assert st == BADP
+    assert rkv.rkv_select_sampled(p, 0, FAKE, FAKE, 300, 8, 10, 1.0, FAKE, stream=0, check=False) == NULL
+    assert rkv.rkv_select_sampled(p, FAKE, 0, FAKE, 300, 8, 10, 1.0, FAKE, stream=0, check=False) == NULL
+    assert rkv.rkv_select_sampled(p, FAKE, FAKE, FAKE, 255, 8, 10, 1.0, FAKE, stream=0,
+                                  check=False) == st_of("RKV_ERR_BAD_SHAPE")
+    for ns in (0, 255, 383):
+        st, out = rkv.rkv_evict_step_sampled(p, layers(), layers(), FAKE, FAKE, FAKE, ns, 8, 10, 1.0, FAKE_WS, need,
+                                             stream=0, check=False)
+        assert st == 0 and out == ns
+
+
 def test_holefill_argument_errors():
     """The hole-filling entry points: NULL or misaligned order, slot range,
     and the no-op below the trigger (nothing launched, fake pointers untouched)."""

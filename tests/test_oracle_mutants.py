@@ -46,6 +46,10 @@ MUTANTS = [
     ("holefill_stayer_moves", "new_order[j] = order[keep[j]];", "new_order[j] = keep[j];"),
     ("holefill_v_not_moved", "std::memcpy((char*)v_rows + (size_t)dst * row_bytes",
      "if (0) std::memcpy((char*)v_rows + (size_t)dst * row_bytes"),
+    ("sampled_gumbel_sign", "- std::log(-std::log((double)uniforms[i]));", "+ std::log(-std::log((double)uniforms[i]));"),
+    ("sampled_no_temperature", "(double)scores[i] / temperature", "(double)scores[i]"),
+    ("sampled_top_k_ignored", "  cand.resize(K);\n", "\n"),
+    ("sampled_score_tie_to_older", "return sa != sb ? sa > sb : a > b;", "return sa != sb ? sa > sb : a < b;"),
     ("holefill_padding_reuses_first_free", "for (int j = 0; j < lead; ++j) new_order[j] = free_rows[m + j];",
      "for (int j = 0; j < lead; ++j) new_order[j] = free_rows[j];"),
 ]
