@@ -366,6 +366,98 @@ def sweep_cpu_baseline(ds, w, budget_s: float = 20.0):
             "ms_per_step": step_s * 1e3, "cpu_seconds": one * n}
 
 
+def sampled_main(args, w):
+    """The step with the sampled selection (no scoring: the scores are a
+    learned scorer's, seeded synthetic here) on the workload's cache: W
+    warm-up steps, K timed steps each between two HIP events, the pristine
+    cache restored and the last-level cache flushed before each; then K
+    selection-only launches for the selection's own time."""
+    import numpy as np
+    import torch
+
+    import synth
+    import redundancy_aware_compression_amd as rkv
+
+    cs = synth.build_cache(w, seed=args.seed)
+    sc, un = synth.sampled_inputs(w, seed=args.seed)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    hip = HipEvents()
+    L = w.buffer if w.buffer < w.budget else w.budget // 2
+    top_k = 2 * (w.budget - L)
+
+    def dev_tensor(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    with torch.cuda.stream(stream):
+        K0, V0, SC, UN = dev_tensor(cs.K), dev_tensor(cs.V), dev_tensor(sc), dev_tensor(un)
+        S0 = torch.from_numpy(cs.seq_start.copy()).to(dev)
+        K, V, S = K0.clone(), V0.clone(), S0.clone()
+        p = rkv.make_params(w.num_layers, w.batch, w.num_kv_heads, w.group, w.capacity, w.budget, w.buffer,
+                            w.obs_window, w.beta, w.lam, w.tau, w.dtype)
+        wsb = rkv.rkv_workspace_bytes(p)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        keep = torch.empty(w.slices * w.budget, dtype=torch.int32, device=dev)
+        flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        flush_out = torch.zeros((), dtype=torch.int64, device=dev)
+        kl, vl = [K[l] for l in range(w.num_layers)], [V[l] for l in range(w.num_layers)]
+        sp = stream.cuda_stream
+
+        def prepare():
+            K.copy_(K0)
+            V.copy_(V0)
+            S.copy_(S0)
+            torch.sum(flush.view(torch.int64), dim=(0,), out=flush_out)
+
+        def step(ev):
+            prepare()
+            hip.record(ev[0], sp)
+            st, ns = rkv.rkv_evict_step_sampled(p, kl, vl, SC, UN, S, cs.n_slots, L, top_k, 1.0, ws, wsb,
+                                                stream=stream)
+            hip.record(ev[1], sp)
+            assert ns == w.budget
+
+        def select_only(ev):
+            prepare()
+            hip.record(ev[0], sp)
+            rkv.rkv_select_sampled(p, SC, UN, S, cs.n_slots, L, top_k, 1.0, keep, stream=stream)
+            hip.record(ev[1], sp)
+
+        warm = hip.create(2)
+        for _ in range(args.warmup):
+            step(warm)
+        evs = [hip.create(2) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step(evs[i])
+        sevs = [hip.create(2) for _ in range(args.steps)]
+        for i in range(args.steps):
+            select_only(sevs[i])
+        torch.cuda.synchronize()
+    step_ms = [hip.elapsed_ms(e[0], e[1]) for e in evs]
+    sel_ms = [hip.elapsed_ms(e[0], e[1]) for e in sevs]
+    for e in evs + sevs + [warm]:
+        hip.destroy(e)
+    mean_ms = sum(step_ms) / len(step_ms)
+    sel_us = sum(sel_ms) / len(sel_ms) * 1e3
+    sel_bytes = w.slices * w.n_slots * 8 + w.slices * w.budget * 4  # scores and uniforms in, keep lists out
+    out = {
+        "metric": METRIC, "value": 1000.0 / mean_ms, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": mean_ms, "us_per_step": mean_ms * 1e3,
+        "us_p10": percentile(step_ms, 10) * 1e3, "us_p90": percentile(step_ms, 90) * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "selection": "sampled", "keep_newest": L, "top_k": top_k, "temperature": 1.0,
+                   "slices": w.slices, "n_slots": w.n_slots, "budget": w.budget, "llc_flush": True,
+                   "seed": args.seed},
+        "kernels": {"select_sampled": {"us": sel_us, "bound": "latency", "bytes": sel_bytes,
+                                       "achieved": sel_bytes / (sel_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                                       "unit": "GB/s"}},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -376,6 +468,9 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="keep inputs warm in the last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rounds", type=int, default=0, help="sweep workloads: rounds to run (default: the recipe's)")
+    ap.add_argument("--selection", choices=["rkv", "sampled"], default="rkv",
+                    help="rkv: the R-KV step (default); sampled: the Top-K + multinomial selection on seeded "
+                         "caller scores (newest `buffer` tokens kept, top_k twice the draw) and the compaction")
     ap.add_argument("--layout", choices=["order-preserving", "holefill"], default="order-preserving",
                     help="compaction layout: the order-preserving step (default) or the hole-filling one with "
                          "its order sidecar")
@@ -395,6 +490,8 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if w.name in SWEEP_WORKLOADS:
         return sweep_main(args, w)
+    if args.selection == "sampled":
+        return sampled_main(args, w)
     cs = synth.build_cache(w, seed=args.seed)
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(device=dev)
