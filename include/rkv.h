@@ -266,6 +266,42 @@ rkv_status rkv_evict_step_sampled(const rkv_params* p, void* const* k_layers, vo
                                   int32_t keep_newest, int32_t top_k, float temperature, void* ws, size_t ws_bytes,
                                   void* stream);
 
+/*
+ * Sentence-level redundancy (SkipKV notes page, summary table rows
+ * "sentence-level KV storage skipping", "final eviction score" and "cache
+ * range monitoring"). A sentence is represented by the mean of its tokens'
+ * last-layer hidden states (the caller's vectors); when a later sentence's
+ * cosine with an earlier one exceeds tau_s, the earlier one is redundant.
+ * rkv_sentence_penalty: penalty[b][i] = the largest cosine of sentence i of
+ * sequence b with a later sentence j < n_sent[b] when it exceeds tau_s, else
+ * 0 (a zero vector is similar to nothing); entries i >= n_sent[b] are 0.
+ *   vectors  float32 [batch][s_max][dim], 16-byte aligned, dim a multiple of
+ *            4 and at most 8192
+ *   n_sent   int32 [batch] (device), sentences per sequence, clamped to s_max
+ *   penalty  out, float32 [batch][s_max]
+ * Errors: RKV_ERR_NULL_ARG, RKV_ERR_MISALIGNED, RKV_ERR_BAD_SHAPE (s_max,
+ * dim), RKV_ERR_BAD_PARAM (tau_s outside [-1, 1]), and those of the params.
+ */
+rkv_status rkv_sentence_penalty(const rkv_params* p, const float* vectors, const int32_t* n_sent, int32_t s_max,
+                                int32_t dim, float tau_s, float* penalty, void* stream);
+
+/*
+ * rkv_evict_step with SkipKV's sentence deduction: the sentence penalties
+ * (rkv_sentence_penalty, into the caller's penalty buffer) are subtracted
+ * from Z of each candidate, by the sentence of its slot, so that tokens of
+ * redundant sentences go before ordinary ones; the kept count stays the
+ * token budget. sent_id: int32 [num_layers][batch][num_kv_heads][capacity],
+ * the sentence index of each slot's token (-1 or >= s_max: none), in/out:
+ * the compaction moves it with the K/V rows (entries of the slots before the
+ * new seq_start become -1), which keeps the sentence map of the cache in
+ * step with its contents. Errors: those of rkv_evict_step and
+ * rkv_sentence_penalty, RKV_ERR_MISALIGNED for sent_id not 4-byte aligned.
+ */
+rkv_status rkv_evict_step_sentences(const rkv_params* p, void* const* k_layers, void* const* v_layers,
+                                    const void* obs_q, int32_t* seq_start, int32_t* n_slots, int32_t* sent_id,
+                                    const float* vectors, const int32_t* n_sent, int32_t s_max, int32_t dim,
+                                    float tau_s, float* penalty, void* ws, size_t ws_bytes, void* stream);
+
 /* Static string naming a status. */
 const char* rkv_status_string(rkv_status st);
 

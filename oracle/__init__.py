@@ -72,6 +72,12 @@ def load_library(path: str):
     L.orc_gather_rows.restype = None
     L.orc_gather_rows.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_void_p]
+    L.orc_slice_penalized.restype = ctypes.c_int32
+    L.orc_slice_penalized.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    L.orc_sentence_penalty.restype = None
+    L.orc_sentence_penalty.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_double,
+                                       ctypes.c_void_p]
     L.orc_select_sampled.restype = ctypes.c_int32
     L.orc_select_sampled.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -112,7 +118,8 @@ class SliceResult:
 
 
 def slice_eval(keys: np.ndarray, queries: np.ndarray, budget: int, obs_window: int = 8, beta: int = 2,
-               lam: float = 0.1, tau: float = 0.5, amb_eps: float = 0.0) -> SliceResult:
+               lam: float = 0.1, tau: float = 0.5, amb_eps: float = 0.0,
+               token_penalty: Optional[np.ndarray] = None) -> SliceResult:
     """Scores and selects one slice.
 
     keys: [N, D]; queries: [G, alpha, D] (or [G*alpha, D]); both bf16 bits
@@ -141,7 +148,13 @@ def slice_eval(keys: np.ndarray, queries: np.ndarray, budget: int, obs_window: i
         res.ambiguous = np.zeros(N, dtype=np.int32)
         for name in ("importance", "rowmean", "counts", "rbar", "R", "Z", "ambiguous"):
             setattr(out, name, getattr(res, name).ctypes.data)
-    kept = lib().orc_slice(ctypes.byref(p), code, keys.ctypes.data, queries.ctypes.data, ctypes.byref(out))
+    if token_penalty is None:
+        kept = lib().orc_slice(ctypes.byref(p), code, keys.ctypes.data, queries.ctypes.data, ctypes.byref(out))
+    else:
+        pen = np.ascontiguousarray(token_penalty, dtype=np.float64)
+        assert pen.shape == (N,)
+        kept = lib().orc_slice_penalized(ctypes.byref(p), code, keys.ctypes.data, queries.ctypes.data,
+                                         pen.ctypes.data, ctypes.byref(out))
     if kept < 0:
         raise ValueError("oracle rejected the slice parameters")
     res.kept = kept
@@ -213,3 +226,11 @@ def select_sampled(scores: np.ndarray, uniforms: np.ndarray, budget: int, keep_n
     if n < 0:
         raise ValueError("invalid sampled-selection parameters")
     return out[:n].copy()
+
+
+def sentence_penalty(vectors: np.ndarray, tau_s: float) -> np.ndarray:
+    """orc_sentence_penalty: vectors [n_sent][dim] float32 -> penalties [n_sent] (double)."""
+    v = np.ascontiguousarray(vectors, dtype=np.float32)
+    out = np.zeros(v.shape[0])
+    lib().orc_sentence_penalty(v.shape[0], v.shape[1], v.ctypes.data, tau_s, out.ctypes.data)
+    return out

@@ -39,8 +39,10 @@ bool valid_slice_params(const orc_slice_params* p, int32_t dtype) {
 
 }  // namespace
 
-extern "C" int32_t orc_slice(const orc_slice_params* p, int32_t dtype, const void* keys, const void* queries,
-                             orc_slice_out* out) {
+namespace {
+
+int32_t slice_impl(const orc_slice_params* p, int32_t dtype, const void* keys, const void* queries,
+                   const double* token_penalty, orc_slice_out* out) {
   if (!valid_slice_params(p, dtype) || !out) return -1;
   const int N = p->n, D = p->head_dim, G = p->group, A = p->obs_window, B = p->budget;
 
@@ -137,6 +139,9 @@ extern "C" int32_t orc_slice(const orc_slice_params* p, int32_t dtype, const voi
   for (int i = 0; i < nc; ++i) {
     R[i] = std::exp(rbar[i] - rmax) / rden;
     Z[i] = p->lambda * imp[i] - (1.0 - p->lambda) * R[i];
+    /* [SKV] SkipKV notes page, summary table row "final eviction score":
+     * tokens of redundant sentences lose their sentence's similarity on top. */
+    if (token_penalty) Z[i] -= token_penalty[i];
   }
 
   /* Selection ([RKV] opening notes: keep the newest 8, score the rest, keep
@@ -166,6 +171,48 @@ extern "C" int32_t orc_slice(const orc_slice_params* p, int32_t dtype, const voi
   if (out->keep)
     for (int j = 0; j < B; ++j) out->keep[j] = kept[j];
   return B;
+}
+
+}  // namespace
+
+extern "C" int32_t orc_slice(const orc_slice_params* p, int32_t dtype, const void* keys, const void* queries,
+                             orc_slice_out* out) {
+  return slice_impl(p, dtype, keys, queries, nullptr, out);
+}
+
+extern "C" int32_t orc_slice_penalized(const orc_slice_params* p, int32_t dtype, const void* keys,
+                                       const void* queries, const double* token_penalty, orc_slice_out* out) {
+  return slice_impl(p, dtype, keys, queries, token_penalty, out);
+}
+
+extern "C" void orc_sentence_penalty(int32_t n_sent, int32_t dim, const float* vectors, double tau_s,
+                                     double* penalty) {
+  /* [SKV] SkipKV notes page, summary table row "sentence-level KV storage
+   * skipping": a sentence is represented by the mean of its tokens' last-layer
+   * hidden states (the vectors given here); when a later sentence's cosine
+   * with an earlier one exceeds the threshold, the earlier one is redundant.
+   * Reading: its penalty is the largest such cosine, 0 if none exceeds. */
+  std::vector<double> nrm(n_sent, 0.0);
+  for (int i = 0; i < n_sent; ++i) {
+    double ss = 0.0;
+    for (int d = 0; d < dim; ++d) ss += (double)vectors[(size_t)i * dim + d] * vectors[(size_t)i * dim + d];
+    nrm[i] = std::sqrt(ss);
+  }
+  for (int i = 0; i < n_sent; ++i) {
+    double best = 0.0;
+    bool any = false;
+    for (int j = i + 1; j < n_sent; ++j) {
+      if (nrm[i] == 0.0 || nrm[j] == 0.0) continue;
+      double dot = 0.0;
+      for (int d = 0; d < dim; ++d) dot += (double)vectors[(size_t)i * dim + d] * vectors[(size_t)j * dim + d];
+      const double c = dot / (nrm[i] * nrm[j]);
+      if (c > tau_s && (!any || c > best)) {
+        best = c;
+        any = true;
+      }
+    }
+    penalty[i] = any ? best : 0.0;
+  }
 }
 
 extern "C" void orc_gather_rows(const void* src, const int32_t* keep, int32_t n_keep, int32_t row_bytes,

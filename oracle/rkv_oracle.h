@@ -9,6 +9,10 @@
  *   [RKV] R-KV notes page, yoonschallenge.tistory.com/1236 (NeurIPS 2025
  *         poster): opening notes, summary table, Q&A part 2 ("why did time
  *         drop less than expected"), cause 3 (per-128-token compression work).
+ *   [SKV] SkipKV notes page, yoonschallenge.tistory.com/1230: summary table
+ *         rows "sentence-level KV storage skipping" and "final eviction score".
+ *   [FKV] ForesightKV explainer, gist.science/ko/paper/2602.03203: technical
+ *         summary (the eviction trigger and the Top-K + multinomial draw).
  * Where the pages are silent (the combination formula, the protection rule,
  * tie order, padding) the readings below are stated at the point of use.
  *
@@ -102,6 +106,16 @@ void orc_gather_rows(const void* src, const int32_t* keep, int32_t n_keep, int32
  */
 int32_t orc_holefill_slice(void* k_rows, void* v_rows, int32_t row_bytes, int32_t budget, int32_t n_slots,
                            const int32_t* keep, int32_t* order);
+
+/* orc_slice with a per-token penalty (N entries, may be NULL) subtracted
+ * from Z of the candidates: SkipKV's sentence-level deduction. */
+int32_t orc_slice_penalized(const orc_slice_params* p, int32_t dtype, const void* keys, const void* queries,
+                            const double* token_penalty, orc_slice_out* out);
+
+/* Sentence redundancy (SkipKV): vectors [n_sent][dim] in generation order;
+ * penalty[i] = the largest cosine of sentence i with a later sentence when
+ * it exceeds tau_s, else 0 (a zero vector has cosine 0 with everything). */
+void orc_sentence_penalty(int32_t n_sent, int32_t dim, const float* vectors, double tau_s, double* penalty);
 
 /*
  * Sampled selection of one slice with n valid tokens (positions 0..n-1):

@@ -27,11 +27,13 @@ from ._binding import (  # noqa: F401
     rkv_evict_step_holefill,
     rkv_evict_step_holefill_timed,
     rkv_evict_step_sampled,
+    rkv_evict_step_sentences,
     rkv_evict_step_timed,
     rkv_last_hip_error,
     rkv_score,
     rkv_select,
     rkv_select_sampled,
+    rkv_sentence_penalty,
     rkv_status_string,
     rkv_workspace_bytes,
     rkv_workspace_keep_offset,

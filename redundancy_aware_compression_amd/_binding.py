@@ -101,6 +101,11 @@ def _lib():
         L.rkv_select_sampled.argtypes = [P, vp, vp, vp, i32, i32, i32, f32, vp, vp]
         L.rkv_evict_step_sampled.restype = ctypes.c_int
         L.rkv_evict_step_sampled.argtypes = [P, vp, vp, vp, vp, vp, ctypes.POINTER(i32), i32, i32, f32, vp, sz, vp]
+        L.rkv_sentence_penalty.restype = ctypes.c_int
+        L.rkv_sentence_penalty.argtypes = [P, vp, vp, i32, i32, f32, vp, vp]
+        L.rkv_evict_step_sentences.restype = ctypes.c_int
+        L.rkv_evict_step_sentences.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(i32), vp, vp, vp, i32, i32, f32, vp,
+                                               vp, sz, vp]
         L.rkv_status_string.restype = ctypes.c_char_p
         L.rkv_status_string.argtypes = [ctypes.c_int]
         L.rkv_last_hip_error.restype = ctypes.c_int
@@ -264,4 +269,26 @@ def rkv_evict_step_sampled(p: RkvParams, k_layers: Sequence, v_layers: Sequence,
                                        temperature, _ptr(ws), ws_bytes, _stream(stream))
     if check:
         _check(st, "rkv_evict_step_sampled")
+    return st, ns.value
+
+
+def rkv_sentence_penalty(p: RkvParams, vectors, n_sent, s_max: int, dim: int, tau_s: float, penalty, stream=None,
+                         check: bool = True) -> int:
+    st = _lib().rkv_sentence_penalty(ctypes.byref(p), _ptr(vectors), _ptr(n_sent), s_max, dim, tau_s, _ptr(penalty),
+                                     _stream(stream))
+    return _check(st, "rkv_sentence_penalty") if check else st
+
+
+def rkv_evict_step_sentences(p: RkvParams, k_layers: Sequence, v_layers: Sequence, obs_q, seq_start, n_slots: int,
+                             sent_id, vectors, n_sent, s_max: int, dim: int, tau_s: float, penalty, ws, ws_bytes: int,
+                             stream=None, check: bool = True):
+    """The eviction step with SkipKV's sentence deduction; returns (status, n_slots after the step)."""
+    ns = ctypes.c_int32(n_slots)
+    st = _lib().rkv_evict_step_sentences(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
+                                         ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(obs_q),
+                                         _ptr(seq_start), ctypes.byref(ns), _ptr(sent_id), _ptr(vectors),
+                                         _ptr(n_sent), s_max, dim, tau_s, _ptr(penalty), _ptr(ws), ws_bytes,
+                                         _stream(stream))
+    if check:
+        _check(st, "rkv_evict_step_sentences")
     return st, ns.value

@@ -159,17 +159,37 @@ rkv_status rkv_compact(const rkv_params* p, void* const* k_layers, void* const* 
 
 namespace {
 
+// SkipKV sentence inputs of the step (see rkv_evict_step_sentences).
+struct SentenceArgs {
+  int32_t* sent_id;
+  const float* vectors;
+  const int32_t* n_sent;
+  int32_t s_max, dim;
+  float tau_s;
+  float* penalty;
+};
+
+rkv_status check_sentences(const SentenceArgs& a) {
+  if (!a.sent_id || !a.vectors || !a.n_sent || !a.penalty) return RKV_ERR_NULL_ARG;
+  if (((uintptr_t)a.vectors & 15u) || ((uintptr_t)a.sent_id & 3u)) return RKV_ERR_MISALIGNED;
+  if (a.s_max < 1 || a.dim < 4 || (a.dim & 3) || a.dim > rkv::kSentMaxDim) return RKV_ERR_BAD_SHAPE;
+  if (!(a.tau_s >= -1.f && a.tau_s <= 1.f)) return RKV_ERR_BAD_PARAM;
+  return RKV_OK;
+}
+
 // The eviction step; with `order` the hole-filling layout (gathered scoring
-// loads, hole-filling compaction), else the order-preserving one.
+// loads, hole-filling compaction), else the order-preserving one; with
+// `sent` SkipKV's sentence deduction and the sentence-id sidecar.
 rkv_status evict_impl(const rkv_params* p, void* const* k_layers, void* const* v_layers, const void* obs_q,
                       int32_t* seq_start, int32_t* order, bool holefill, int32_t* n_slots, void* ws, size_t ws_bytes,
-                      void* stream, void* const* stage_events) {
+                      void* stream, void* const* stage_events, const SentenceArgs* sent = nullptr) {
   rkv_status st = check_params(p);
   if (st != RKV_OK) return st;
   if ((st = check_layers(p, (const void* const*)k_layers)) != RKV_OK) return st;
   if ((st = check_layers(p, (const void* const*)v_layers)) != RKV_OK) return st;
   if (!obs_q || !seq_start || !n_slots || !ws || (holefill && !order)) return RKV_ERR_NULL_ARG;
   if (holefill && rkv::holefill_lds_bytes(p->budget) > rkv::kHolefillMaxLds) return RKV_ERR_UNSUPPORTED;
+  if (sent && (st = check_sentences(*sent)) != RKV_OK) return st;
   if (!aligned16(obs_q) || ((uintptr_t)ws & 255u) || ((uintptr_t)order & 3u)) return RKV_ERR_MISALIGNED;
   const int32_t ns = *n_slots;
   if (ns < 0 || ns > p->capacity) return RKV_ERR_BAD_SHAPE;
@@ -185,16 +205,21 @@ rkv_status evict_impl(const rkv_params* p, void* const* k_layers, void* const* v
     return (int)hipEventRecord((hipEvent_t)stage_events[i], (hipStream_t)stream);
   };
   RKV_TRY(mark(0));
+  if (sent)
+    RKV_TRY(rkv::launch_sentence_penalty(sent->vectors, sent->n_sent, p->batch, sent->s_max, sent->dim, sent->tau_s,
+                                         sent->penalty, stream));
   RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, holefill ? order : nullptr, w.importance, w.rowmean,
                            w.counts, stream));
   RKV_TRY(mark(1));
   RKV_TRY(rkv::launch_select(g, w.importance, nullptr, w.counts, w.rowmean, seq_start, w.keep, nullptr, nullptr,
-                             stream));
+                             stream, sent ? sent->penalty : nullptr, sent ? sent->sent_id : nullptr,
+                             sent ? sent->s_max : 0));
   RKV_TRY(mark(2));
   if (holefill)
     RKV_TRY(rkv::launch_compact_holefill(g, p->dtype, kl, vl, w.keep, order, seq_start, stream));
   else
     RKV_TRY(rkv::launch_compact(g, p->dtype, kl, vl, w.keep, seq_start, stream));
+  if (sent) RKV_TRY(rkv::launch_compact_ids(g, w.keep, sent->sent_id, stream));
   RKV_TRY(mark(3));
   *n_slots = p->budget;
   return RKV_OK;
@@ -293,6 +318,26 @@ rkv_status rkv_evict_step_sampled(const rkv_params* p, void* const* k_layers, vo
                               make_layers(p, (const void* const*)v_layers), w.keep, seq_start, stream));
   *n_slots = p->budget;
   return RKV_OK;
+}
+
+rkv_status rkv_sentence_penalty(const rkv_params* p, const float* vectors, const int32_t* n_sent, int32_t s_max,
+                                int32_t dim, float tau_s, float* penalty, void* stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  int32_t dummy_id = 0;
+  SentenceArgs a{&dummy_id, vectors, n_sent, s_max, dim, tau_s, penalty};
+  if ((st = check_sentences(a)) != RKV_OK) return st;
+  RKV_TRY(rkv::launch_sentence_penalty(vectors, n_sent, p->batch, s_max, dim, tau_s, penalty, stream));
+  return RKV_OK;
+}
+
+rkv_status rkv_evict_step_sentences(const rkv_params* p, void* const* k_layers, void* const* v_layers,
+                                    const void* obs_q, int32_t* seq_start, int32_t* n_slots, int32_t* sent_id,
+                                    const float* vectors, const int32_t* n_sent, int32_t s_max, int32_t dim,
+                                    float tau_s, float* penalty, void* ws, size_t ws_bytes, void* stream) {
+  SentenceArgs a{sent_id, vectors, n_sent, s_max, dim, tau_s, penalty};
+  return evict_impl(p, k_layers, v_layers, obs_q, seq_start, nullptr, false, n_slots, ws, ws_bytes, stream, nullptr,
+                    &a);
 }
 
 }  // extern "C"

@@ -80,7 +80,11 @@ int launch_select_sampled(const Geom& g, const float* scores, const float* unifo
                           int keep_newest, int top_k, float temperature, int32_t* keep, void* stream);
 int launch_select(const Geom& g, const float* importance, const float* redundancy, const int32_t* counts,
                   const float* rowmean, const int32_t* seq_start, int32_t* keep, float* z_out, float* r_out,
-                  void* stream);
+                  void* stream, const float* sent_pen = nullptr, const int32_t* sent_id = nullptr, int s_max = 0);
+int launch_sentence_penalty(const float* vectors, const int32_t* n_sent, int batch, int s_max, int dim, float tau_s,
+                            float* penalty, void* stream);
+int launch_compact_ids(const Geom& g, const int32_t* keep, int32_t* ids, void* stream);
+constexpr int kSentMaxDim = 8192;
 // dynamic LDS of the hole-filling compaction; launches keep it within 64 KB
 size_t holefill_lds_bytes(int budget);
 constexpr size_t kHolefillMaxLds = 65536 - 2048;

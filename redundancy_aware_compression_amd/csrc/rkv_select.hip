@@ -84,14 +84,19 @@ __device__ inline void radix_kth(const uint32_t* keys, int n, int k, int* hist, 
 
 // FROM_COUNTS: redundancy = counts < beta ? 0 : rowmean (the eviction step);
 // otherwise read the given redundancy array (the standalone select call).
-template <bool FROM_COUNTS>
+// PEN: SkipKV's sentence deduction (SkipKV notes page, summary table row
+// "final eviction score"): Z of a candidate loses the penalty of its slot's
+// sentence, sent_pen[b][sent_id[slot]] (ids outside [0, s_max): none).
+template <bool FROM_COUNTS, bool PEN>
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(Geom g, const float* __restrict__ importance,
                                                                 const float* __restrict__ redundancy,
                                                                 const int32_t* __restrict__ counts,
                                                                 const float* __restrict__ rowmean,
                                                                 const int32_t* __restrict__ seq_start,
                                                                 int32_t* __restrict__ keep, float* __restrict__ z_out,
-                                                                float* __restrict__ r_out) {
+                                                                float* __restrict__ r_out,
+                                                                const float* __restrict__ sent_pen,
+                                                                const int32_t* __restrict__ sent_id, int s_max) {
   __shared__ uint32_t keys[RKV_MAX_CAPACITY];
   __shared__ int hist[256];
   __shared__ float fscr[16];
@@ -136,7 +141,11 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Geom g, const fl
   const float inv = 1.f / sum;
   for (int i = tid; i < nc; i += nt) {
     const float R = fk[i] * inv;
-    const float Z = g.lambda * importance[base + i] - (1.f - g.lambda) * R;
+    float Z = g.lambda * importance[base + i] - (1.f - g.lambda) * R;
+    if (PEN) {
+      const int sid = sent_id[(size_t)slice * g.capacity + s0 + i];
+      Z -= (sid >= 0 && sid < s_max) ? sent_pen[(size_t)b * s_max + sid] : 0.f;
+    }
     keys[i] = order_key(Z);
     if (z_out) z_out[base + i] = Z;
     if (r_out) r_out[base + i] = R;
@@ -307,16 +316,20 @@ int launch_select_sampled(const Geom& g, const float* scores, const float* unifo
 
 int launch_select(const Geom& g, const float* importance, const float* redundancy, const int32_t* counts,
                   const float* rowmean, const int32_t* seq_start, int32_t* keep, float* z_out, float* r_out,
-                  void* stream) {
+                  void* stream, const float* sent_pen, const int32_t* sent_id, int s_max) {
   const int slices = g.L * g.batch * g.H;
   if (slices == 0) return 0;
   hipStream_t s = (hipStream_t)stream;
-  if (counts)
-    hipLaunchKernelGGL(select_kernel<true>, dim3(slices), dim3(kSelectThreads), 0, s, g, importance, redundancy,
-                       counts, rowmean, seq_start, keep, z_out, r_out);
+  const dim3 grid(slices), block(kSelectThreads);
+  if (counts && sent_pen)
+    hipLaunchKernelGGL((select_kernel<true, true>), grid, block, 0, s, g, importance, redundancy, counts, rowmean,
+                       seq_start, keep, z_out, r_out, sent_pen, sent_id, s_max);
+  else if (counts)
+    hipLaunchKernelGGL((select_kernel<true, false>), grid, block, 0, s, g, importance, redundancy, counts, rowmean,
+                       seq_start, keep, z_out, r_out, sent_pen, sent_id, s_max);
   else
-    hipLaunchKernelGGL(select_kernel<false>, dim3(slices), dim3(kSelectThreads), 0, s, g, importance, redundancy,
-                       counts, rowmean, seq_start, keep, z_out, r_out);
+    hipLaunchKernelGGL((select_kernel<false, false>), grid, block, 0, s, g, importance, redundancy, counts,
+                       rowmean, seq_start, keep, z_out, r_out, sent_pen, sent_id, s_max);
   return (int)hipGetLastError();
 }
 

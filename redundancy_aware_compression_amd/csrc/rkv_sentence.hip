@@ -1,0 +1,109 @@
+// Sentence-level redundancy (SkipKV notes page, yoonschallenge.tistory.com/
+// 1230, summary table rows "sentence-level KV storage skipping", "final
+// eviction score" and "cache range monitoring"): a sentence is represented by
+// the mean of its tokens' last-layer hidden states (the caller's vectors);
+// when a later sentence's cosine with an earlier one exceeds a threshold the
+// earlier one is redundant, and its tokens lose that similarity on the
+// eviction score, so they go before ordinary tokens. Each cached slot carries
+// its token's sentence id, a sidecar that moves with the slot's K/V rows so
+// that sentence scores keep landing on the right cache entries after evictions.
+#include "rkv_device.hpp"
+
+namespace rkv {
+
+constexpr int kSentThreads = 256;
+
+// One work-group per (sentence i, sequence b): penalty[b][i] = the largest
+// cosine of sentence i with a later sentence j < n_sent[b] when it exceeds
+// tau_s, else 0 (a zero vector is similar to nothing). fp32 dot products over
+// dim (a multiple of 4, at most kSentMaxDim); sentence i's vector is staged in
+// LDS and the waves take the later sentences in turn.
+__global__ __launch_bounds__(kSentThreads) void sentence_penalty_kernel(const float* __restrict__ vectors,
+                                                                        const int32_t* __restrict__ n_sent,
+                                                                        int s_max, int dim, float tau_s,
+                                                                        float* __restrict__ penalty) {
+  extern __shared__ __align__(16) float hv[];
+  __shared__ float red[kSentThreads / 64];
+  const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int n = n_sent[b];
+  n = n < 0 ? 0 : (n > s_max ? s_max : n);
+  float* out = penalty + (size_t)b * s_max + i;
+  if (i >= n) {
+    if (tid == 0) *out = 0.f;
+    return;
+  }
+  const float4* vi = (const float4*)(vectors + ((size_t)b * s_max + i) * dim);
+  float ss = 0.f;
+  for (int d = tid; d < dim / 4; d += kSentThreads) {
+    const float4 x = vi[d];
+    ((float4*)hv)[d] = x;
+    ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) red[w] = ss;
+  __syncthreads();
+  float ni = 0.f;
+#pragma unroll
+  for (int k = 0; k < kSentThreads / 64; ++k) ni += red[k];
+  ni = sqrtf(ni);
+  float best = -INFINITY;  // the wave's largest cosine above tau_s
+  for (int j = i + 1 + w; j < n; j += kSentThreads / 64) {
+    const float4* vj = (const float4*)(vectors + ((size_t)b * s_max + j) * dim);
+    float dot = 0.f, sj = 0.f;
+    for (int d = lane; d < dim / 4; d += 64) {
+      const float4 x = ((const float4*)hv)[d], y = vj[d];
+      dot += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+      sj += y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
+    }
+    dot = wave_sum(dot);
+    sj = wave_sum(sj);
+    if (ni > 0.f && sj > 0.f) {
+      const float c = dot / (ni * sqrtf(sj));
+      if (c > tau_s) best = fmaxf(best, c);
+    }
+  }
+  __syncthreads();  // red is reused
+  if (lane == 0) red[w] = best;
+  __syncthreads();
+  if (tid == 0) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kSentThreads / 64; ++k) m = fmaxf(m, red[k]);
+    *out = m > -INFINITY ? m : 0.f;
+  }
+}
+
+// The sidecar's compaction: ids[j] <- ids[keep[j]] for every slice (order-
+// preserving, the layout of the K/V compaction), -1 where keep[j] < 0. All
+// reads go through LDS before any write, so the in-place gather is safe.
+__global__ __launch_bounds__(kSentThreads) void compact_ids_kernel(Geom g, const int32_t* __restrict__ keep,
+                                                                   int32_t* __restrict__ ids) {
+  extern __shared__ __align__(16) int32_t stage[];
+  const int slice = blockIdx.x, tid = threadIdx.x, B = g.budget;
+  const int32_t* krow = keep + (size_t)slice * B;
+  int32_t* irow = ids + (size_t)slice * g.capacity;
+  for (int j = tid; j < B; j += kSentThreads) {
+    const int k = krow[j];
+    stage[j] = (k >= 0 && k < g.n_slots) ? irow[k] : -1;
+  }
+  __syncthreads();
+  for (int j = tid; j < B; j += kSentThreads) irow[j] = stage[j];
+}
+
+int launch_sentence_penalty(const float* vectors, const int32_t* n_sent, int batch, int s_max, int dim, float tau_s,
+                            float* penalty, void* stream) {
+  if (batch == 0 || s_max == 0) return 0;
+  hipLaunchKernelGGL(sentence_penalty_kernel, dim3(s_max, batch), dim3(kSentThreads), (size_t)dim * 4,
+                     (hipStream_t)stream, vectors, n_sent, s_max, dim, tau_s, penalty);
+  return (int)hipGetLastError();
+}
+
+int launch_compact_ids(const Geom& g, const int32_t* keep, int32_t* ids, void* stream) {
+  const int slices = g.L * g.batch * g.H;
+  if (slices == 0) return 0;
+  hipLaunchKernelGGL(compact_ids_kernel, dim3(slices), dim3(kSentThreads), (size_t)g.budget * 4,
+                     (hipStream_t)stream, g, keep, ids);
+  return (int)hipGetLastError();
+}
+
+}  // namespace rkv

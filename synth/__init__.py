@@ -32,7 +32,7 @@ BF16 = 0
 F32 = 1
 
 # tensor ids of the per-slice streams
-T_KEYS, T_VALUES, T_QUERIES, T_LENGTHS, T_MIX, T_SCORES, T_UNIFORMS = 0, 1, 2, 3, 4, 5, 6
+T_KEYS, T_VALUES, T_QUERIES, T_LENGTHS, T_MIX, T_SCORES, T_UNIFORMS, T_SENT = 0, 1, 2, 3, 4, 5, 6, 7
 
 BF16_NAN = 0x7FC0
 BF16_CANARY = 0x7F81  # a signalling-NaN pattern no generator or copy produces
@@ -539,3 +539,52 @@ def sampled_inputs(w: Workload, seed: int = 0):
                                     w.n_slots)
                 L.synth_fill_uniform_open(stream_key(seed, w.wid, T_UNIFORMS, l, b, h), _ptr(un[l, b, h]), w.n_slots)
     return sc, un
+
+
+
+@dataclass
+class Sentences:
+    """Synthetic sentence structure of a cache (SkipKV's inputs): sequence b's
+    valid tokens split into n_sent[b] sentences of 8..40 tokens in generation
+    order; vectors[b][i] stands for the mean of sentence i's last-layer hidden
+    states; sent_id[l][b][h][slot] is the sentence of the slot's token (-1 for
+    padding and unused slots)."""
+
+    vectors: np.ndarray  # [batch][s_max][dim] float32
+    n_sent: np.ndarray  # [batch] int32
+    sent_id: np.ndarray  # [L][b][H][capacity] int32
+
+
+def sentences(cs: CacheSet, dim: int = 1024, repeat_p: float = 0.25, noise: float = 0.2, seed: int = 0) -> Sentences:
+    """Sentence boundaries, vectors and the per-slot sentence sidecar for a
+    cache. Vectors are N(0, 1); with probability repeat_p a sentence's vector
+    is instead a noisy copy (noise sigma per element) of a uniformly chosen
+    earlier sentence's, so that earlier sentence becomes redundant (cosine
+    about 1 / sqrt(1 + noise^2))."""
+    w = cs.w
+    rng = np.random.default_rng(np.uint64(stream_key(seed, w.wid, T_SENT, 0, 0, 0)))
+    bounds = []
+    for b in range(w.batch):
+        n, t, ids = int(cs.lengths[b]), 0, []
+        k = 0
+        while t < n:
+            ln = int(rng.integers(8, 41))
+            ids.extend([k] * min(ln, n - t))
+            t += ln
+            k += 1
+        bounds.append(np.asarray(ids, np.int32))
+    n_sent = np.array([int(x.max()) + 1 if len(x) else 0 for x in bounds], np.int32)
+    s_max = max(1, int(n_sent.max()))
+    vec = np.zeros((w.batch, s_max, dim), np.float32)
+    for b in range(w.batch):
+        for i in range(n_sent[b]):
+            if i > 0 and rng.random() < repeat_p:
+                src = int(rng.integers(0, i))
+                vec[b, i] = vec[b, src] + noise * rng.standard_normal(dim).astype(np.float32)
+            else:
+                vec[b, i] = rng.standard_normal(dim).astype(np.float32)
+    sid = np.full((w.num_layers, w.batch, w.num_kv_heads, w.capacity), -1, np.int32)
+    for b in range(w.batch):
+        s0 = int(cs.seq_start[b])
+        sid[:, b, :, s0:s0 + len(bounds[b])] = bounds[b]
+    return Sentences(vec, n_sent, sid)

@@ -468,6 +468,50 @@ def check_sampled_scale_invariance():
         assert np.array_equal(a, b)
 
 
+def check_sentence_penalty_closed_forms():
+    """Sentence redundancy: exact cosines of small vectors. (1,0) against the
+    later (0.75,1) and (3,4) has cosine 0.6 > 0.5; (0.75,1) against (3,4)
+    has 1; (3,4) against (0,-1) has -0.8; the last sentence has no later one.
+    Scaled copies have cosine 1, orthogonal vectors 0, a zero vector 0."""
+    v = np.array([[1, 0], [0.75, 1], [3, 4], [0, -1]], np.float32)
+    pen = oracle.sentence_penalty(v, 0.5)
+    assert abs(pen[0] - 0.6) < 1e-15 and abs(pen[1] - 1.0) < 1e-15
+    assert pen[2] == 0.0 and pen[3] == 0.0
+    assert np.all(oracle.sentence_penalty(v, 0.99) == np.array([0.0, 1.0, 0.0, 0.0]))
+    rng = np.random.default_rng(31)
+    base = rng.standard_normal((1, 64)).astype(np.float32)
+    copies = np.concatenate([base * np.float32(c) for c in (1, 2, 0.5, 4)])
+    assert np.allclose(oracle.sentence_penalty(copies, 0.5), [1, 1, 1, 0], atol=1e-12)
+    eye = np.eye(5, 8, dtype=np.float32)
+    assert np.all(oracle.sentence_penalty(eye, 0.0) == 0.0)  # cosine 0 is not above 0
+    z = np.vstack([np.zeros((1, 8), np.float32), eye[:1] * np.float32(3), eye[:1]])
+    assert oracle.sentence_penalty(z, 0.5).tolist() == [0.0, 1.0, 0.0]  # a zero vector is never similar
+
+
+def check_penalized_selection():
+    """The sentence penalty enters Z as a subtraction on the candidates: a zero
+    penalty reproduces the plain selection, a constant one leaves the kept
+    set unchanged, and a penalty larger than any score gap evicts the
+    penalised candidates first while budget allows."""
+    rng = np.random.default_rng(32)
+    for _ in range(20):
+        n, d, g, a = int(rng.integers(24, 48)), 16, 2, 4
+        B = int(rng.integers(a + 4, n - 2))
+        k, q = _rand_slice(int(rng.integers(1 << 30)), n, d, g, a)
+        plain = oracle.slice_eval(k, q, budget=B, obs_window=a)
+        zero = oracle.slice_eval(k, q, budget=B, obs_window=a, token_penalty=np.zeros(n))
+        assert np.array_equal(plain.keep, zero.keep) and np.array_equal(plain.Z, zero.Z)
+        const = oracle.slice_eval(k, q, budget=B, obs_window=a, token_penalty=np.full(n, 0.25))
+        assert np.array_equal(plain.keep, const.keep)
+        nc = n - a
+        hit = rng.choice(nc, size=int(rng.integers(1, n - B + 1)), replace=False)
+        pen = np.zeros(n)
+        pen[hit] = 10.0
+        r = oracle.slice_eval(k, q, budget=B, obs_window=a, token_penalty=pen)
+        assert not (set(hit.tolist()) & set(r.keep.tolist())), "a penalised candidate was kept"
+        assert np.allclose(r.Z[:nc], plain.Z[:nc] - pen[:nc], atol=0)
+
+
 ALL_CHECKS = [
     check_hand_cases,
     check_lambda1_textbook,
@@ -488,4 +532,6 @@ ALL_CHECKS = [
     check_sampled_equal_scores,
     check_sampled_inclusion_probabilities,
     check_sampled_scale_invariance,
+    check_sentence_penalty_closed_forms,
+    check_penalized_selection,
 ]

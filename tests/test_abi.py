@@ -138,6 +138,28 @@ def test_sampled_argument_errors():
         assert st == 0 and out == ns
 
 
+def test_sentence_argument_errors():
+    p = P()
+    need = rkv.rkv_workspace_bytes(p)
+    NULL, MIS, SHAPE, BADP = (st_of(x) for x in ("RKV_ERR_NULL_ARG", "RKV_ERR_MISALIGNED", "RKV_ERR_BAD_SHAPE",
+                                                   "RKV_ERR_BAD_PARAM"))
+    assert rkv.rkv_sentence_penalty(p, 0, FAKE, 16, 64, 0.8, FAKE, stream=0, check=False) == NULL
+    assert rkv.rkv_sentence_penalty(p, FAKE + 8, FAKE, 16, 64, 0.8, FAKE, stream=0, check=False) == MIS
+    for s_max, dim in ((0, 64), (16, 2), (16, 66), (16, 8196)):
+        assert rkv.rkv_sentence_penalty(p, FAKE, FAKE, s_max, dim, 0.8, FAKE, stream=0, check=False) == SHAPE
+    assert rkv.rkv_sentence_penalty(p, FAKE, FAKE, 16, 64, 1.5, FAKE, stream=0, check=False) == BADP
+    st, _ = rkv.rkv_evict_step_sentences(p, layers(), layers(), FAKE, FAKE, 384, 0, FAKE, FAKE, 16, 64, 0.8, FAKE,
+                                         FAKE_WS, need, stream=0, check=False)
+    assert st == NULL
+    st, _ = rkv.rkv_evict_step_sentences(p, layers(), layers(), FAKE, FAKE, 384, FAKE + 2, FAKE, FAKE, 16, 64, 0.8,
+                                         FAKE, FAKE_WS, need, stream=0, check=False)
+    assert st == MIS
+    for ns in (0, 383):  # below the trigger: nothing launched
+        st, out = rkv.rkv_evict_step_sentences(p, layers(), layers(), FAKE, FAKE, ns, FAKE, FAKE, FAKE, 16, 64, 0.8,
+                                               FAKE, FAKE_WS, need, stream=0, check=False)
+        assert st == 0 and out == ns
+
+
 def test_holefill_argument_errors():
     """The hole-filling entry points: NULL or misaligned order, slot range,
     and the no-op below the trigger (nothing launched, fake pointers untouched)."""

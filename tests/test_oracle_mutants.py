@@ -50,6 +50,10 @@ MUTANTS = [
     ("sampled_no_temperature", "(double)scores[i] / temperature", "(double)scores[i]"),
     ("sampled_top_k_ignored", "  cand.resize(K);\n", "\n"),
     ("sampled_score_tie_to_older", "return sa != sb ? sa > sb : a > b;", "return sa != sb ? sa > sb : a < b;"),
+    ("sentence_penalty_added", "if (token_penalty) Z[i] -= token_penalty[i];",
+     "if (token_penalty) Z[i] += token_penalty[i];"),
+    ("sentence_earlier_not_later", "for (int j = i + 1; j < n_sent; ++j) {", "for (int j = 0; j < i; ++j) {"),
+    ("sentence_threshold_ignored", "if (c > tau_s && (!any || c > best)) {", "if ((!any || c > best)) {"),
     ("holefill_padding_reuses_first_free", "for (int j = 0; j < lead; ++j) new_order[j] = free_rows[m + j];",
      "for (int j = 0; j < lead; ++j) new_order[j] = free_rows[j];"),
 ]
