@@ -366,6 +366,96 @@ def sweep_cpu_baseline(ds, w, budget_s: float = 20.0):
             "ms_per_step": step_s * 1e3, "cpu_seconds": one * n}
 
 
+def sentences_main(args, w):
+    """The R-KV step with SkipKV's sentence deduction (rkv_evict_step_sentences)
+    on the workload's cache and synthetic sentences (8..40 tokens, 1024-wide
+    vectors, a quarter of them noisy repeats): W warm-up steps, K timed steps
+    between two HIP events, cache, start slots and sentence sidecar restored
+    and the last-level cache flushed before each; then K penalty-only launches
+    for the sentence kernel's own time."""
+    import numpy as np
+    import torch
+
+    import synth
+    import redundancy_aware_compression_amd as rkv
+
+    cs = synth.build_cache(w, seed=args.seed)
+    se = synth.sentences(cs, seed=args.seed)
+    s_max, dim = se.vectors.shape[1], se.vectors.shape[2]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    hip = HipEvents()
+
+    def dev_tensor(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    with torch.cuda.stream(stream):
+        K0, V0, Q, ID0 = dev_tensor(cs.K), dev_tensor(cs.V), dev_tensor(cs.Q), dev_tensor(se.sent_id)
+        VEC, NS = dev_tensor(se.vectors), dev_tensor(se.n_sent)
+        S0 = torch.from_numpy(cs.seq_start.copy()).to(dev)
+        K, V, S, ID = K0.clone(), V0.clone(), S0.clone(), ID0.clone()
+        PEN = torch.empty(w.batch * s_max, dtype=torch.float32, device=dev)
+        p = rkv.make_params(w.num_layers, w.batch, w.num_kv_heads, w.group, w.capacity, w.budget, w.buffer,
+                            w.obs_window, w.beta, w.lam, w.tau, w.dtype)
+        wsb = rkv.rkv_workspace_bytes(p)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        flush_out = torch.zeros((), dtype=torch.int64, device=dev)
+        kl, vl = [K[l] for l in range(w.num_layers)], [V[l] for l in range(w.num_layers)]
+        sp = stream.cuda_stream
+
+        def prepare():
+            K.copy_(K0)
+            V.copy_(V0)
+            S.copy_(S0)
+            ID.copy_(ID0)
+            torch.sum(flush.view(torch.int64), dim=(0,), out=flush_out)
+
+        def step(ev):
+            prepare()
+            hip.record(ev[0], sp)
+            st, ns = rkv.rkv_evict_step_sentences(p, kl, vl, Q, S, cs.n_slots, ID, VEC, NS, s_max, dim, 0.8, PEN,
+                                                  ws, wsb, stream=stream)
+            hip.record(ev[1], sp)
+            assert ns == w.budget
+
+        def penalty_only(ev):
+            prepare()
+            hip.record(ev[0], sp)
+            rkv.rkv_sentence_penalty(p, VEC, NS, s_max, dim, 0.8, PEN, stream=stream)
+            hip.record(ev[1], sp)
+
+        warm = hip.create(2)
+        for _ in range(args.warmup):
+            step(warm)
+        evs = [hip.create(2) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            step(evs[i])
+        pevs = [hip.create(2) for _ in range(args.steps)]
+        for i in range(args.steps):
+            penalty_only(pevs[i])
+        torch.cuda.synchronize()
+    step_ms = [hip.elapsed_ms(e[0], e[1]) for e in evs]
+    pen_ms = [hip.elapsed_ms(e[0], e[1]) for e in pevs]
+    for e in evs + pevs + [warm]:
+        hip.destroy(e)
+    mean_ms = sum(step_ms) / len(step_ms)
+    out = {
+        "metric": METRIC, "value": 1000.0 / mean_ms, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": mean_ms, "us_per_step": mean_ms * 1e3,
+        "us_p10": percentile(step_ms, 10) * 1e3, "us_p90": percentile(step_ms, 90) * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "selection": "sentences", "sentences": int(se.n_sent.sum()),
+                   "vector_dim": dim, "tau_s": 0.8, "slices": w.slices, "n_slots": w.n_slots, "llc_flush": True,
+                   "seed": args.seed},
+        "kernels": {"sentence_penalty": {"us": sum(pen_ms) / len(pen_ms) * 1e3, "bound": "latency"}},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def sampled_main(args, w):
     """The step with the sampled selection (no scoring: the scores are a
     learned scorer's, seeded synthetic here) on the workload's cache: W
@@ -468,9 +558,10 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="keep inputs warm in the last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rounds", type=int, default=0, help="sweep workloads: rounds to run (default: the recipe's)")
-    ap.add_argument("--selection", choices=["rkv", "sampled"], default="rkv",
+    ap.add_argument("--selection", choices=["rkv", "sampled", "sentences"], default="rkv",
                     help="rkv: the R-KV step (default); sampled: the Top-K + multinomial selection on seeded "
-                         "caller scores (newest `buffer` tokens kept, top_k twice the draw) and the compaction")
+                         "caller scores (newest `buffer` tokens kept, top_k twice the draw) and the compaction; "
+                         "sentences: the R-KV step with SkipKV's sentence deduction on synthetic sentences")
     ap.add_argument("--layout", choices=["order-preserving", "holefill"], default="order-preserving",
                     help="compaction layout: the order-preserving step (default) or the hole-filling one with "
                          "its order sidecar")
@@ -492,6 +583,8 @@ def main():
         return sweep_main(args, w)
     if args.selection == "sampled":
         return sampled_main(args, w)
+    if args.selection == "sentences":
+        return sentences_main(args, w)
     cs = synth.build_cache(w, seed=args.seed)
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(device=dev)

@@ -12,12 +12,14 @@
 namespace rkv {
 
 constexpr int kSentThreads = 256;
+constexpr int kSentBatch = 4;
+constexpr int kSentChunk = 4;  // float4 per lane per sentence in one round of loads
 
 // One work-group per (sentence i, sequence b): penalty[b][i] = the largest
 // cosine of sentence i with a later sentence j < n_sent[b] when it exceeds
 // tau_s, else 0 (a zero vector is similar to nothing). fp32 dot products over
 // dim (a multiple of 4, at most kSentMaxDim); sentence i's vector is staged in
-// LDS and the waves take the later sentences in turn.
+// LDS and the waves take the later sentences in batches.
 __global__ __launch_bounds__(kSentThreads) void sentence_penalty_kernel(const float* __restrict__ vectors,
                                                                         const int32_t* __restrict__ n_sent,
                                                                         int s_max, int dim, float tau_s,
@@ -47,19 +49,49 @@ __global__ __launch_bounds__(kSentThreads) void sentence_penalty_kernel(const fl
   for (int k = 0; k < kSentThreads / 64; ++k) ni += red[k];
   ni = sqrtf(ni);
   float best = -INFINITY;  // the wave's largest cosine above tau_s
-  for (int j = i + 1 + w; j < n; j += kSentThreads / 64) {
-    const float4* vj = (const float4*)(vectors + ((size_t)b * s_max + j) * dim);
-    float dot = 0.f, sj = 0.f;
-    for (int d = lane; d < dim / 4; d += 64) {
-      const float4 x = ((const float4*)hv)[d], y = vj[d];
-      dot += x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
-      sj += y.x * y.x + y.y * y.y + y.z * y.z + y.w * y.w;
+  // Each wave takes kSentBatch later sentences at a time; their loads are
+  // independent, so a batch costs about one memory round trip. Indexes past
+  // the last sentence re-read sentence n - 1 and are discarded.
+  for (int j0 = i + 1 + w * kSentBatch; j0 < n; j0 += kSentThreads / 64 * kSentBatch) {
+    float dot[kSentBatch], sj[kSentBatch];
+    const float4* vj[kSentBatch];
+#pragma unroll
+    for (int u = 0; u < kSentBatch; ++u) {
+      dot[u] = 0.f;
+      sj[u] = 0.f;
+      vj[u] = (const float4*)(vectors + ((size_t)b * s_max + min(j0 + u, n - 1)) * dim);
     }
-    dot = wave_sum(dot);
-    sj = wave_sum(sj);
-    if (ni > 0.f && sj > 0.f) {
-      const float c = dot / (ni * sqrtf(sj));
-      if (c > tau_s) best = fmaxf(best, c);
+    for (int d0 = 0; d0 < dim / 4; d0 += 64 * kSentChunk) {
+      // all loads of the chunk first; a clamped index and a 0/1 mask cover
+      // the tail past dim
+      float4 y[kSentBatch][kSentChunk], x[kSentChunk];
+      float mk[kSentChunk];
+#pragma unroll
+      for (int c = 0; c < kSentChunk; ++c) {
+        const int d = d0 + c * 64 + lane, dc = min(d, dim / 4 - 1);
+        mk[c] = d < dim / 4 ? 1.f : 0.f;
+#pragma unroll
+        for (int u = 0; u < kSentBatch; ++u) y[u][c] = vj[u][dc];
+        x[c] = ((const float4*)hv)[dc];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of their uses
+#pragma unroll
+      for (int c = 0; c < kSentChunk; ++c) {
+#pragma unroll
+        for (int u = 0; u < kSentBatch; ++u) {
+          const float4 a = y[u][c];
+          dot[u] += mk[c] * (x[c].x * a.x + x[c].y * a.y + x[c].z * a.z + x[c].w * a.w);
+          sj[u] += mk[c] * (a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kSentBatch; ++u) {
+      const float dt = wave_sum(dot[u]), sn = wave_sum(sj[u]);
+      if (j0 + u < n && ni > 0.f && sn > 0.f) {
+        const float c = dt / (ni * sqrtf(sn));
+        if (c > tau_s) best = fmaxf(best, c);
+      }
     }
   }
   __syncthreads();  // red is reused
