@@ -81,6 +81,10 @@ def load_library(path: str):
     L.orc_select_sampled.restype = ctypes.c_int32
     L.orc_select_sampled.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    L.orc_decode_attention.restype = ctypes.c_int32
+    L.orc_decode_attention.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p]
     L.orc_holefill_slice.restype = ctypes.c_int32
     L.orc_holefill_slice.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
@@ -234,3 +238,24 @@ def sentence_penalty(vectors: np.ndarray, tau_s: float) -> np.ndarray:
     out = np.zeros(v.shape[0])
     lib().orc_sentence_penalty(v.shape[0], v.shape[1], v.ctypes.data, tau_s, out.ctypes.data)
     return out
+
+
+def decode_attention(keys: np.ndarray, values: np.ndarray, queries: np.ndarray):
+    """Decode attention of one slice: keys, values [n][D] and the newest
+    token's queries [G][D] (bf16 as uint16, or float32). Returns (out [G][D],
+    weights [G][n]) in float64."""
+    keys, values, queries = (np.ascontiguousarray(a) for a in (keys, values, queries))
+    dt = _dtype_code(keys)
+    if _dtype_code(values) != dt or _dtype_code(queries) != dt:
+        raise ValueError("keys, values and queries must share a dtype")
+    n, D = keys.shape
+    G = queries.shape[0]
+    if values.shape != (n, D) or queries.shape != (G, D):
+        raise ValueError("shape mismatch")
+    out = np.zeros((G, D), np.float64)
+    w = np.zeros((G, n), np.float64)
+    rc = lib().orc_decode_attention(n, D, G, dt, keys.ctypes.data, values.ctypes.data, queries.ctypes.data,
+                                    out.ctypes.data, w.ctypes.data)
+    if rc != 0:
+        raise ValueError("orc_decode_attention rejected its arguments")
+    return out, w

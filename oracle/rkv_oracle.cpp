@@ -185,6 +185,42 @@ extern "C" int32_t orc_slice_penalized(const orc_slice_params* p, int32_t dtype,
   return slice_impl(p, dtype, keys, queries, token_penalty, out);
 }
 
+/* Decode attention of one slice, the step that runs at every generated token
+ * ([RKV] Q&A part 2, cause 4: fusing attention, importance scoring and
+ * eviction into one kernel). The newest token's G query heads attend to the
+ * slice's n keys, its own key included: w_gj = softmax over j of
+ * q_g.k_j / sqrt(D), and out_g = sum_j w_gj v_j. The weights are the
+ * attention rows that the importance averages over the observation window,
+ * so a decode step can hand them over as it computes them. */
+extern "C" int32_t orc_decode_attention(int32_t n, int32_t head_dim, int32_t group, int32_t dtype, const void* keys,
+                                        const void* values, const void* queries, double* out, double* weights) {
+  if (n < 0 || head_dim <= 0 || group <= 0 || !out) return -1;
+  if (dtype != ORC_BF16 && dtype != ORC_F32) return -1;
+  const int D = head_dim;
+  for (int64_t i = 0; i < (int64_t)group * D; ++i) out[i] = 0.0;
+  if (n == 0) return 0;
+  if (!keys || !values || !queries) return -1;
+  const double inv_sqrt_d = 1.0 / std::sqrt((double)D);
+  std::vector<double> lg(n);
+  for (int g = 0; g < group; ++g) {
+    double mx = -INFINITY;
+    for (int j = 0; j < n; ++j) {
+      double s = 0.0;
+      for (int d = 0; d < D; ++d) s += load(queries, dtype, (int64_t)g * D + d) * load(keys, dtype, (int64_t)j * D + d);
+      lg[j] = inv_sqrt_d * s;
+      mx = std::max(mx, lg[j]);
+    }
+    double den = 0.0;
+    for (int j = 0; j < n; ++j) den += std::exp(lg[j] - mx);
+    for (int j = 0; j < n; ++j) {
+      const double w = std::exp(lg[j] - mx) / den;
+      if (weights) weights[(int64_t)g * n + j] = w;
+      for (int d = 0; d < D; ++d) out[(int64_t)g * D + d] += w * load(values, dtype, (int64_t)j * D + d);
+    }
+  }
+  return 0;
+}
+
 extern "C" void orc_sentence_penalty(int32_t n_sent, int32_t dim, const float* vectors, double tau_s,
                                      double* penalty) {
   /* [SKV] SkipKV notes page, summary table row "sentence-level KV storage

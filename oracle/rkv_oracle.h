@@ -112,6 +112,14 @@ int32_t orc_holefill_slice(void* k_rows, void* v_rows, int32_t row_bytes, int32_
 int32_t orc_slice_penalized(const orc_slice_params* p, int32_t dtype, const void* keys, const void* queries,
                             const double* token_penalty, orc_slice_out* out);
 
+/* Decode attention of one slice with n keys (the newest token's own
+ * included): out[g][d] = sum_j w[g][j] v[j][d], w[g] = softmax over j of
+ * q[g].k[j] / sqrt(head_dim). keys, values [n][head_dim], queries
+ * [group][head_dim] in dtype; out [group][head_dim] and weights [group][n]
+ * (nullable) in double. n == 0 gives out = 0. Returns 0, -1 on bad arguments. */
+int32_t orc_decode_attention(int32_t n, int32_t head_dim, int32_t group, int32_t dtype, const void* keys,
+                             const void* values, const void* queries, double* out, double* weights);
+
 /* Sentence redundancy (SkipKV): vectors [n_sent][dim] in generation order;
  * penalty[i] = the largest cosine of sentence i with a later sentence when
  * it exceeds tau_s, else 0 (a zero vector has cosine 0 with everything). */

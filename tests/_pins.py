@@ -92,6 +92,11 @@ def check_hand_cases():
             check_hand_case(case, pad_to=128)
 
 
+def _bf16_f64(bits):
+    """bf16 bit patterns (uint16) widened exactly to float64."""
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
 def _rand_slice(seed, n, d, g, alpha, dtype="bf16", scale=1.0):
     rng = np.random.default_rng(seed)
     k = (rng.standard_normal((n, d)) * scale).astype(np.float32)
@@ -512,6 +517,83 @@ def check_penalized_selection():
         assert np.allclose(r.Z[:nc], plain.Z[:nc] - pen[:nc], atol=0)
 
 
+def check_decode_attention_textbook():
+    """Decode attention against torch float64's scaled_dot_product_attention
+    (default scale 1/sqrt(D)) and torch.softmax for the weights, on bf16 and
+    fp32 slices with n from 1 to 70 keys and G from 1 to 5 query heads."""
+    import torch
+
+    rng = np.random.default_rng(40)
+    for it, (n, d, g) in enumerate([(1, 16, 1), (2, 8, 3), (37, 16, 4), (70, 32, 5), (64, 128, 4)]):
+        k = rng.standard_normal((n, d)).astype(np.float32)
+        v = rng.standard_normal((n, d)).astype(np.float32)
+        q = rng.standard_normal((g, d)).astype(np.float32)
+        for bf in (False, True):
+            if bf:
+                kb, vb, qb = synth.bf16_bits(k), synth.bf16_bits(v), synth.bf16_bits(q)
+                kd, vd, qd = (_bf16_f64(x) for x in (kb, vb, qb))
+            else:
+                kb, vb, qb = k, v, q
+                kd, vd, qd = (x.astype(np.float64) for x in (k, v, q))
+            out, w = oracle.decode_attention(kb, vb, qb)
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(qd)[None], torch.from_numpy(kd)[None], torch.from_numpy(vd)[None])[0]
+            wref = torch.softmax(torch.from_numpy(qd) @ torch.from_numpy(kd).T / math.sqrt(d), dim=-1)
+            _close(out, ref.numpy(), 1e-12, f"decode attention output, case {it} bf16={bf}")
+            _close(w, wref.numpy(), 1e-12, f"decode attention weights, case {it} bf16={bf}")
+
+
+def check_decode_attention_special_cases():
+    """One key: its value comes back exactly with weight 1. Identical keys (or
+    a zero query): uniform weights 1/n and the mean of the values. Unit keys
+    against a query of 32 on one axis (D = 16): logit 8 for that key, 0 for
+    the rest, weights e^8 / (e^8 + n - 1) and 1 / (e^8 + n - 1). No keys:
+    the output is 0."""
+    rng = np.random.default_rng(41)
+    d = 16
+    v1 = rng.standard_normal((1, d)).astype(np.float32)
+    k1 = rng.standard_normal((1, d)).astype(np.float32)
+    q = rng.standard_normal((3, d)).astype(np.float32)
+    out, w = oracle.decode_attention(k1, v1, q)
+    assert np.all(w == 1.0) and np.all(out == v1.astype(np.float64))
+    n = 9
+    krow = rng.standard_normal((1, d)).astype(np.float32)
+    vals = rng.standard_normal((n, d)).astype(np.float32)
+    out, w = oracle.decode_attention(np.repeat(krow, n, 0), vals, q)
+    _close(w, np.full((3, n), 1.0 / n), 1e-15, "identical keys: uniform weights")
+    _close(out, np.repeat(vals.astype(np.float64).mean(0, keepdims=True), 3, 0), 1e-14, "identical keys: mean")
+    out, w = oracle.decode_attention(rng.standard_normal((n, d)).astype(np.float32), vals,
+                                     np.zeros((2, d), np.float32))
+    _close(w, np.full((2, n), 1.0 / n), 1e-15, "zero query: uniform weights")
+    e = np.eye(n, d, dtype=np.float32)
+    qq = np.zeros((1, d), np.float32)
+    qq[0, 4] = 32.0  # logit 32 / 4 = 8 for key 4, 0 for the others
+    out, w = oracle.decode_attention(e, vals, qq)
+    want = math.exp(8) / (math.exp(8) + n - 1)
+    assert abs(w[0, 4] - want) < 1e-15 and abs(w[0, 0] - 1 / (math.exp(8) + n - 1)) < 1e-15
+    out, w = oracle.decode_attention(np.zeros((0, d), np.float32), np.zeros((0, d), np.float32), q)
+    assert out.shape == (3, d) and np.all(out == 0)
+
+
+def check_captured_importance():
+    """The importance that decode attention can capture: the weights of the
+    alpha window steps (the step of the token at position N - alpha + t sees
+    keys 0 .. N - alpha + t, its own included), summed per key, divided by
+    alpha and maxed over the group, equal the oracle's importance, which is
+    pinned on its own by the hand cases and the textbook pipeline."""
+    for seed, (n, d, g, a, budget) in enumerate([(40, 16, 3, 4, 24), (70, 32, 5, 8, 40), (33, 8, 1, 1, 20),
+                                                 (50, 16, 2, 6, 30)]):
+        k_bits, q_bits = _rand_slice(300 + seed, n, d, g, a)
+        v_bits = synth.bf16_bits(np.random.default_rng(400 + seed).standard_normal((n, d)).astype(np.float32))
+        acc = np.zeros((g, n))
+        for t in range(a):
+            m = n - a + t + 1
+            _, w = oracle.decode_attention(k_bits[:m], v_bits[:m], q_bits[:, t])
+            acc[:, :m] += w
+        ref = oracle.slice_eval(k_bits, q_bits, budget=budget, obs_window=a)
+        _close(acc.max(0) / a, ref.importance, 1e-15, f"captured importance, case {seed}")
+
+
 ALL_CHECKS = [
     check_hand_cases,
     check_lambda1_textbook,
@@ -534,4 +616,7 @@ ALL_CHECKS = [
     check_sampled_scale_invariance,
     check_sentence_penalty_closed_forms,
     check_penalized_selection,
+    check_decode_attention_textbook,
+    check_decode_attention_special_cases,
+    check_captured_importance,
 ]

@@ -54,6 +54,11 @@ MUTANTS = [
      "if (token_penalty) Z[i] += token_penalty[i];"),
     ("sentence_earlier_not_later", "for (int j = i + 1; j < n_sent; ++j) {", "for (int j = 0; j < i; ++j) {"),
     ("sentence_threshold_ignored", "if (c > tau_s && (!any || c > best)) {", "if ((!any || c > best)) {"),
+    ("decode_no_attention_scale", "lg[j] = inv_sqrt_d * s;", "lg[j] = s;"),
+    ("decode_drops_newest_key", "    for (int j = 0; j < n; ++j) den += std::exp(lg[j] - mx);",
+     "    for (int j = 0; j < n - 1; ++j) den += std::exp(lg[j] - mx);"),
+    ("decode_query_of_head_zero", "load(queries, dtype, (int64_t)g * D + d)", "load(queries, dtype, (int64_t)d)"),
+    ("decode_value_of_key_zero", "load(values, dtype, (int64_t)j * D + d)", "load(values, dtype, (int64_t)d)"),
     ("holefill_padding_reuses_first_free", "for (int j = 0; j < lead; ++j) new_order[j] = free_rows[m + j];",
      "for (int j = 0; j < lead; ++j) new_order[j] = free_rows[j];"),
 ]
