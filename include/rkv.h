@@ -302,6 +302,51 @@ rkv_status rkv_evict_step_sentences(const rkv_params* p, void* const* k_layers, 
                                     const float* vectors, const int32_t* n_sent, int32_t s_max, int32_t dim,
                                     float tau_s, float* penalty, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Decode attention with importance capture. R-KV's importance is the
+ * attention that the newest obs_window queries pay each cached token (R-KV
+ * notes page, summary table row "importance computation"); those rows are
+ * what the decode steps compute anyway, and the notes name fusing attention,
+ * importance scoring and eviction into one kernel as a way to cut the cost
+ * of compression (Q&A part 2, cause 4).
+ *
+ * rkv_decode_attention: the newest token of every sequence attends to the
+ * sequence's valid slots [seq_start[b], n_slots), its own K/V row (slot
+ * n_slots - 1) included: for each query head, w = softmax over those slots
+ * of q.k / sqrt(head_dim) and out = sum_j w_j v_j.
+ *   k_layers, v_layers  HOST [num_layers] device pointers, the cache layout
+ *                       of rkv_evict_step (16-byte aligned)
+ *   q        [num_layers][batch][num_kv_heads * group][head_dim], cache dtype,
+ *            16-byte aligned (query head hq belongs to KV head hq / group)
+ *   out      out, float32 [num_layers][batch][num_kv_heads * group][head_dim];
+ *            0 for a sequence with no valid slot
+ *   imp_acc  NULL, or float32 [num_layers][batch][num_kv_heads][group][capacity]
+ *            (in/out): w is ADDED at the slot of each key. Zero it before the
+ *            first of the obs_window decode steps that precede an eviction
+ *            (and after every eviction, whose compaction moves the slots), and
+ *            pass it on those steps only; rkv_evict_step_captured then reads it.
+ * Errors: those of the params and layers, RKV_ERR_NULL_ARG, RKV_ERR_MISALIGNED,
+ * RKV_ERR_BAD_SHAPE (n_slots outside [1, capacity]), RKV_ERR_UNSUPPORTED
+ * (group > 8, or group * max(n_slots, 1024) * 4 bytes of weights above 159 KiB).
+ */
+rkv_status rkv_decode_attention(const rkv_params* p, const void* const* k_layers, const void* const* v_layers,
+                                const void* q, const int32_t* seq_start, int32_t n_slots, float* out,
+                                float* imp_acc, void* stream);
+
+/*
+ * rkv_evict_step with the importance taken from imp_acc (filled by
+ * rkv_decode_attention over the obs_window decode steps before the trigger):
+ * I = max over the group of imp_acc / obs_window, which equals the importance
+ * that rkv_evict_step computes from those steps' queries. The queries are not
+ * read. Everything else (redundancy, selection, compaction, n_slots and
+ * seq_start updates, no-op below budget + buffer) is rkv_evict_step's.
+ * Errors: those of rkv_evict_step; RKV_ERR_NULL_ARG for imp_acc NULL,
+ * RKV_ERR_MISALIGNED for imp_acc not 4-byte aligned.
+ */
+rkv_status rkv_evict_step_captured(const rkv_params* p, void* const* k_layers, void* const* v_layers,
+                                   const float* imp_acc, int32_t* seq_start, int32_t* n_slots, void* ws,
+                                   size_t ws_bytes, void* stream);
+
 /* Static string naming a status. */
 const char* rkv_status_string(rkv_status st);
 

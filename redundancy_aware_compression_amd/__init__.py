@@ -28,6 +28,8 @@ from ._binding import (  # noqa: F401
     rkv_evict_step_holefill_timed,
     rkv_evict_step_sampled,
     rkv_evict_step_sentences,
+    rkv_evict_step_captured,
+    rkv_decode_attention,
     rkv_evict_step_timed,
     rkv_last_hip_error,
     rkv_score,

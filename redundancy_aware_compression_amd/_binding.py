@@ -106,6 +106,10 @@ def _lib():
         L.rkv_evict_step_sentences.restype = ctypes.c_int
         L.rkv_evict_step_sentences.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(i32), vp, vp, vp, i32, i32, f32, vp,
                                                vp, sz, vp]
+        L.rkv_decode_attention.restype = ctypes.c_int
+        L.rkv_decode_attention.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp]
+        L.rkv_evict_step_captured.restype = ctypes.c_int
+        L.rkv_evict_step_captured.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(i32), vp, sz, vp]
         L.rkv_status_string.restype = ctypes.c_char_p
         L.rkv_status_string.argtypes = [ctypes.c_int]
         L.rkv_last_hip_error.restype = ctypes.c_int
@@ -291,4 +295,27 @@ def rkv_evict_step_sentences(p: RkvParams, k_layers: Sequence, v_layers: Sequenc
                                          _stream(stream))
     if check:
         _check(st, "rkv_evict_step_sentences")
+    return st, ns.value
+
+
+def rkv_decode_attention(p: RkvParams, k_layers: Sequence, v_layers: Sequence, q, seq_start, n_slots: int, out,
+                         imp_acc=None, stream=None, check: bool = True) -> int:
+    """Decode attention of the newest token; with imp_acc the weights are added into it."""
+    st = _lib().rkv_decode_attention(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
+                                     ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(q), _ptr(seq_start),
+                                     n_slots, _ptr(out), _ptr(imp_acc) if imp_acc is not None else None,
+                                     _stream(stream))
+    return _check(st, "rkv_decode_attention") if check else st
+
+
+def rkv_evict_step_captured(p: RkvParams, k_layers: Sequence, v_layers: Sequence, imp_acc, seq_start, n_slots: int,
+                            ws, ws_bytes: int, stream=None, check: bool = True):
+    """The eviction step with the importance captured by decode attention; returns
+    (status, n_slots after the step)."""
+    ns = ctypes.c_int32(n_slots)
+    st = _lib().rkv_evict_step_captured(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
+                                        ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(imp_acc),
+                                        _ptr(seq_start), ctypes.byref(ns), _ptr(ws), ws_bytes, _stream(stream))
+    if check:
+        _check(st, "rkv_evict_step_captured")
     return st, ns.value

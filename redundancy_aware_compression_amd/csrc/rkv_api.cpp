@@ -182,15 +182,17 @@ rkv_status check_sentences(const SentenceArgs& a) {
 // `sent` SkipKV's sentence deduction and the sentence-id sidecar.
 rkv_status evict_impl(const rkv_params* p, void* const* k_layers, void* const* v_layers, const void* obs_q,
                       int32_t* seq_start, int32_t* order, bool holefill, int32_t* n_slots, void* ws, size_t ws_bytes,
-                      void* stream, void* const* stage_events, const SentenceArgs* sent = nullptr) {
+                      void* stream, void* const* stage_events, const SentenceArgs* sent = nullptr,
+                      const float* imp_acc = nullptr) {
   rkv_status st = check_params(p);
   if (st != RKV_OK) return st;
   if ((st = check_layers(p, (const void* const*)k_layers)) != RKV_OK) return st;
   if ((st = check_layers(p, (const void* const*)v_layers)) != RKV_OK) return st;
-  if (!obs_q || !seq_start || !n_slots || !ws || (holefill && !order)) return RKV_ERR_NULL_ARG;
+  if ((!obs_q && !imp_acc) || !seq_start || !n_slots || !ws || (holefill && !order)) return RKV_ERR_NULL_ARG;
   if (holefill && rkv::holefill_lds_bytes(p->budget) > rkv::kHolefillMaxLds) return RKV_ERR_UNSUPPORTED;
   if (sent && (st = check_sentences(*sent)) != RKV_OK) return st;
-  if (!aligned16(obs_q) || ((uintptr_t)ws & 255u) || ((uintptr_t)order & 3u)) return RKV_ERR_MISALIGNED;
+  if (!aligned16(obs_q) || ((uintptr_t)ws & 255u) || ((uintptr_t)order & 3u) || ((uintptr_t)imp_acc & 3u))
+    return RKV_ERR_MISALIGNED;
   const int32_t ns = *n_slots;
   if (ns < 0 || ns > p->capacity) return RKV_ERR_BAD_SHAPE;
   rkv::Workspace w = rkv::carve(*p, ws);
@@ -209,7 +211,7 @@ rkv_status evict_impl(const rkv_params* p, void* const* k_layers, void* const* v
     RKV_TRY(rkv::launch_sentence_penalty(sent->vectors, sent->n_sent, p->batch, sent->s_max, sent->dim, sent->tau_s,
                                          sent->penalty, stream));
   RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, holefill ? order : nullptr, w.importance, w.rowmean,
-                           w.counts, stream));
+                           w.counts, stream, imp_acc));
   RKV_TRY(mark(1));
   RKV_TRY(rkv::launch_select(g, w.importance, nullptr, w.counts, w.rowmean, seq_start, w.keep, nullptr, nullptr,
                              stream, sent ? sent->penalty : nullptr, sent ? sent->sent_id : nullptr,
@@ -338,6 +340,32 @@ rkv_status rkv_evict_step_sentences(const rkv_params* p, void* const* k_layers, 
   SentenceArgs a{sent_id, vectors, n_sent, s_max, dim, tau_s, penalty};
   return evict_impl(p, k_layers, v_layers, obs_q, seq_start, nullptr, false, n_slots, ws, ws_bytes, stream, nullptr,
                     &a);
+}
+
+rkv_status rkv_decode_attention(const rkv_params* p, const void* const* k_layers, const void* const* v_layers,
+                                const void* q, const int32_t* seq_start, int32_t n_slots, float* out,
+                                float* imp_acc, void* stream) {
+  rkv_status st = check_params(p);
+  if (st != RKV_OK) return st;
+  if ((st = check_layers(p, k_layers)) != RKV_OK) return st;
+  if ((st = check_layers(p, v_layers)) != RKV_OK) return st;
+  if (!q || !seq_start || !out) return RKV_ERR_NULL_ARG;
+  if (!aligned16(q) || ((uintptr_t)out & 3u) || ((uintptr_t)imp_acc & 3u)) return RKV_ERR_MISALIGNED;
+  if (n_slots < 1 || n_slots > p->capacity) return RKV_ERR_BAD_SHAPE;
+  if (p->group > rkv::kDecMaxG || rkv::decode_lds_bytes(p->group, n_slots) > rkv::kDecMaxLds)
+    return RKV_ERR_UNSUPPORTED;
+  const rkv::Geom g = make_geom(p, n_slots);
+  RKV_TRY(rkv::launch_decode(g, p->dtype, make_layers(p, k_layers), make_layers(p, v_layers), q, seq_start, out,
+                             imp_acc, stream));
+  return RKV_OK;
+}
+
+rkv_status rkv_evict_step_captured(const rkv_params* p, void* const* k_layers, void* const* v_layers,
+                                   const float* imp_acc, int32_t* seq_start, int32_t* n_slots, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  if (!imp_acc) return RKV_ERR_NULL_ARG;
+  return evict_impl(p, k_layers, v_layers, nullptr, seq_start, nullptr, false, n_slots, ws, ws_bytes, stream,
+                    nullptr, nullptr, imp_acc);
 }
 
 }  // extern "C"

@@ -1,0 +1,289 @@
+// Decode attention with importance capture. R-KV scores each cached token by
+// the attention that the newest alpha queries pay it (R-KV notes page,
+// summary table row "importance computation"), and the notes name fusing
+// attention, importance scoring and eviction into one kernel as the way to
+// cut the cost of compression (Q&A part 2, cause 4). The decode step already
+// computes those attention rows: this kernel computes the newest token's
+// attention output and, during the alpha steps before an eviction, adds each
+// query head's normalised weights into a per-slot accumulator. The eviction
+// step then reads its importance from the accumulator instead of recomputing
+// the observation queries' attention.
+#include "rkv_device.hpp"
+
+namespace rkv {
+
+constexpr int kDecThreads = 512;
+constexpr int kDecWaves = kDecThreads / 64;
+
+// A lane holds one 16-byte chunk of a row: LPR lanes cover a row, RPI rows
+// are covered by one load instruction of the wave (fully coalesced).
+template <typename T>
+struct DecLanes;
+template <>
+struct DecLanes<bf16_t> {
+  static constexpr int LPR = 16, EPL = 8;
+  __device__ static void widen(const uint4& x, float* f) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <>
+struct DecLanes<float> {
+  static constexpr int LPR = 32, EPL = 4;
+  __device__ static void widen(const uint4& x, float* f) {
+    f[0] = __uint_as_float(x.x);
+    f[1] = __uint_as_float(x.y);
+    f[2] = __uint_as_float(x.z);
+    f[3] = __uint_as_float(x.w);
+  }
+};
+
+// Sum over the LPR lanes of a row: quad swaps, half-row and row mirrors
+// (every lane of the 16 receives the total), then lanes 16 apart for fp32.
+template <int LPR>
+__device__ inline float row_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  if constexpr (LPR == 32) v += __shfl_xor(v, 16);
+  return v;
+}
+
+// The element of a G-register array selected by a runtime index, as a chain
+// of selects. Each element passes through an empty asm so that the chain
+// cannot be turned back into an indexed access, which would put the array in
+// scratch memory.
+template <int G>
+__device__ inline float pick(const float (&a)[G], int i) {
+  float r = a[0];
+#pragma unroll
+  for (int k = 1; k < G; ++k) {
+    float ak = a[k];
+    asm volatile("" : "+v"(ak));
+    r = i == k ? ak : r;
+  }
+  return r;
+}
+
+// One work-group per slice (layer, sequence, KV head) with N valid slots
+// [s0, n_slots): for each of its G query heads, w = softmax over the N keys
+// of q.k / sqrt(D) and out = sum_j w_j v_j (fp32). With acc, the weights are
+// added to acc[slice][g][s0 + j]. LDS (dynamic): the logits, then the
+// weights, as [N][G]; afterwards the waves' partial outputs [8][G][128].
+template <typename T, int G>
+__global__ __launch_bounds__(kDecThreads) void decode_kernel(Geom g, LayerPtrs k, LayerPtrs v,
+                                                             const void* __restrict__ q,
+                                                             const int32_t* __restrict__ seq_start,
+                                                             float* __restrict__ out, float* __restrict__ acc) {
+  using DL = DecLanes<T>;
+  constexpr int LPR = DL::LPR, EPL = DL::EPL, RPI = 64 / LPR;
+  constexpr int RB = kHeadDim * (int)sizeof(T);
+  constexpr int U = G * EPL <= 32 ? 8 : 4;  // row loads per lane in flight (fewer with more query registers)
+  constexpr int STEP = kDecWaves * RPI * U;  // rows per round of the work-group
+  extern __shared__ __align__(16) float lw[];
+  __shared__ float red_m[kDecWaves][G], red_s[kDecWaves][G];
+
+  const int slice = blockIdx.x;
+  int l, b, h, s0, N;
+  slice_coords(g, slice, l, b, h);
+  seq_range(g, seq_start, b, s0, N);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane % LPR, rr = lane / LPR;
+  float* o_out = out + (size_t)slice * G * kHeadDim;
+  if (N == 0) {
+    for (int e = tid; e < G * kHeadDim; e += kDecThreads) o_out[e] = 0.f;
+    return;
+  }
+  const char* kb = row_ptr<T>(k.p[l], g, b, h, s0);
+  const char* vb = row_ptr<T>(v.p[l], g, b, h, s0);
+
+  // the lane's chunk of each query row, scaled so that logits are in log2 units
+  const float qs = 1.4426950408889634f / sqrtf((float)kHeadDim);
+  float qf[G][EPL];
+  {
+    const char* qb = (const char*)q + (size_t)slice * G * RB;
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      DL::widen(*(const uint4*)(qb + gi * RB + c * 16), qf[gi]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) qf[gi][e] *= qs;
+    }
+  }
+
+  // ---- logits: lane c < G of each row stores query c's logit and keeps its max
+  float mrun = -INFINITY;
+  for (int j0 = wave * RPI * U; j0 < N; j0 += STEP) {
+    uint4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = min(j0 + u * RPI + rr, N - 1);  // rows past the slice re-read its last row, unused
+      x[u] = *(const uint4*)(kb + (size_t)row * RB + c * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // all loads of the round before their uses
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[EPL];
+      DL::widen(x[u], kf);
+      float part[G];
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s = fmaf(qf[gi][e], kf[e], s);
+        part[gi] = row_sum<LPR>(s);
+      }
+      const int row = j0 + u * RPI + rr;
+      if (c < G && row < N) {
+        const float lg = pick<G>(part, c);
+        lw[row * G + c] = lg;
+        mrun = fmaxf(mrun, lg);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = LPR; o < 64; o <<= 1) mrun = fmaxf(mrun, __shfl_xor(mrun, o));
+  if (rr == 0 && c < G) red_m[wave][c] = mrun;
+  __syncthreads();
+  float m[G];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    m[gi] = red_m[0][gi];
+#pragma unroll
+    for (int w = 1; w < kDecWaves; ++w) m[gi] = fmaxf(m[gi], red_m[w][gi]);
+  }
+
+  // ---- weights (unnormalised) and their sums
+  float ssum[G];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) ssum[gi] = 0.f;
+  for (int e = tid; e < N * G; e += kDecThreads) {
+    const int gi = e % G;
+    const float p = exp2f(lw[e] - pick<G>(m, gi));
+    lw[e] = p;
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) ssum[gg] += gi == gg ? p : 0.f;
+  }
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    const float s = wave_sum(ssum[gi]);
+    if (lane == 0) red_s[wave][gi] = s;
+  }
+  __syncthreads();  // the weights are in LDS and the sums in red_s
+  float inv[G];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) s += red_s[w][gi];
+    inv[gi] = 1.f / s;
+  }
+
+  // ---- output: o[g] = sum_j p_j v_j over the lane's rows and dims
+  float o[G][EPL];
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[gi][e] = 0.f;
+  for (int j0 = wave * RPI * U; j0 < N; j0 += STEP) {
+    uint4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = min(j0 + u * RPI + rr, N - 1);
+      x[u] = *(const uint4*)(vb + (size_t)row * RB + c * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = j0 + u * RPI + rr;
+      const bool ok = row < N;
+      const int rc = ok ? row : N - 1;  // in-bounds index for rows past the slice, weight 0
+      float vf[EPL];
+      DL::widen(x[u], vf);
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const float p = ok ? lw[rc * G + gi] : 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[gi][e] = fmaf(p, vf[e], o[gi][e]);
+      }
+    }
+  }
+
+  // ---- capture: acc[g][j] += w_gj
+  if (acc) {
+    float* ab = acc + (size_t)slice * G * g.capacity + s0;
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+      for (int j = tid; j < N; j += kDecThreads) ab[(size_t)gi * g.capacity + j] += lw[j * G + gi] * inv[gi];
+  }
+
+  // ---- combine the rows of the wave, then the waves
+#pragma unroll
+  for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+#pragma unroll
+      for (int s = LPR; s < 64; s <<= 1) o[gi][e] += __shfl_xor(o[gi][e], s);
+  __syncthreads();  // every wave is done with the weights
+  if (rr == 0) {
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) lw[(wave * G + gi) * kHeadDim + c * EPL + e] = o[gi][e];
+  }
+  __syncthreads();
+  for (int e = tid; e < G * kHeadDim; e += kDecThreads) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) s += lw[w * G * kHeadDim + e];
+    o_out[e] = s * pick<G>(inv, e / kHeadDim);
+  }
+}
+
+size_t decode_lds_bytes(int group, int n_slots) {
+  const int rows = n_slots > kDecWaves * kHeadDim ? n_slots : kDecWaves * kHeadDim;
+  return (size_t)group * rows * 4;
+}
+
+template <typename T, int G>
+static int launch_decode_g(const Geom& g, const LayerPtrs& k, const LayerPtrs& v, const void* q,
+                           const int32_t* seq_start, float* out, float* acc, hipStream_t s) {
+  const size_t lds = decode_lds_bytes(G, g.n_slots);
+  if (lds > 65536) {
+    const int err = (int)hipFuncSetAttribute((const void*)decode_kernel<T, G>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err) return err;
+  }
+  hipLaunchKernelGGL((decode_kernel<T, G>), dim3(g.L * g.batch * g.H), dim3(kDecThreads), lds, s, g, k, v, q,
+                     seq_start, out, acc);
+  return (int)hipGetLastError();
+}
+
+template <typename T>
+static int launch_decode_t(const Geom& g, const LayerPtrs& k, const LayerPtrs& v, const void* q,
+                           const int32_t* seq_start, float* out, float* acc, hipStream_t s) {
+  switch (g.G) {
+    case 1: return launch_decode_g<T, 1>(g, k, v, q, seq_start, out, acc, s);
+    case 2: return launch_decode_g<T, 2>(g, k, v, q, seq_start, out, acc, s);
+    case 3: return launch_decode_g<T, 3>(g, k, v, q, seq_start, out, acc, s);
+    case 4: return launch_decode_g<T, 4>(g, k, v, q, seq_start, out, acc, s);
+    case 5: return launch_decode_g<T, 5>(g, k, v, q, seq_start, out, acc, s);
+    case 6: return launch_decode_g<T, 6>(g, k, v, q, seq_start, out, acc, s);
+    case 7: return launch_decode_g<T, 7>(g, k, v, q, seq_start, out, acc, s);
+    case 8: return launch_decode_g<T, 8>(g, k, v, q, seq_start, out, acc, s);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+int launch_decode(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const void* q,
+                  const int32_t* seq_start, float* out, float* acc, void* stream) {
+  if (g.L * g.batch * g.H == 0) return 0;
+  hipStream_t s = (hipStream_t)stream;
+  return dtype == RKV_BF16 ? launch_decode_t<bf16_t>(g, k, v, q, seq_start, out, acc, s)
+                           : launch_decode_t<float>(g, k, v, q, seq_start, out, acc, s);
+}
+
+}  // namespace rkv

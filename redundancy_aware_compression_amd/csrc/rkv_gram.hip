@@ -273,12 +273,18 @@ struct SRows<float> {
 // slot v < budget is stored at physical slot order[v], v >= budget at v (the
 // layout the hole-filling compaction keeps). The row loads gather physical
 // rows in virtual order; everything else works in virtual slots.
-template <typename T, bool GATHER>
+// CAPT: the importance comes from the attention weights that decode steps
+// captured, imp_acc [slices][G][capacity] (sums over the observation window):
+// I = max over the group of the sum / alpha. The queries are not read and the
+// logit work is left out; only with GATHER = false.
+template <typename T, bool GATHER, bool CAPT>
 __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k, const void* __restrict__ obs_q,
                                                             const int32_t* __restrict__ seq_start,
                                                             const int32_t* __restrict__ order,
+                                                            const float* __restrict__ imp_acc,
                                                             float* __restrict__ importance,
                                                             float* __restrict__ rowmean, int32_t* __restrict__ counts) {
+  static_assert(!(GATHER && CAPT), "captured importance is indexed by virtual slot only without GATHER");
   using S = Stage<T>;
   using TL = Tile16<T>;
   constexpr int RB = S::RB;
@@ -429,10 +435,12 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
     }
     issue_row(0, poff[0], 0);
     cursor_step();
-    issue_rows<T>(lds_addr(q_lds),
-                  make_desc((const char*)obs_q + ((size_t)(l * g.batch + b) * g.H + h) * (size_t)g.qrows * RB,
-                            (uint32_t)g.qrows * RB),
-                  voff, 0u, wave);
+    // (the queries come before ROW(1), so no wait on a later block counts them)
+    if constexpr (!CAPT)
+      issue_rows<T>(lds_addr(q_lds),
+                    make_desc((const char*)obs_q + ((size_t)(l * g.batch + b) * g.H + h) * (size_t)g.qrows * RB,
+                              (uint32_t)g.qrows * RB),
+                    voff, 0u, wave);
 #pragma unroll
     for (int X = 1; X < S::COUNT; ++X) {
       if (X < pro_n) {
@@ -490,6 +498,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
       for (int e = 0; e < 16; ++e) run[e] = fmaf(x[e], inv, run[e]);
       // logit tiles t = wave, wave + 8: keys 16 (t % 4) .. of the block,
       // query rows 16 (t / 4) ..; lane: query row (lane & 15), keys 4 (lane >> 4) + r
+      if constexpr (CAPT) return;
       const bool edge = blk * kRowBlock + kRowBlock > N - alpha;  // causal or past-the-slice keys inside
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -537,7 +546,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int t = wave + 8 * u;
-    if (t < 4 * nqt16) TL::load(qtile[u], q_lds, 16 * (t >> 2) + (lane & 15), lane >> 4);
+    if (!CAPT && t < 4 * nqt16) TL::load(qtile[u], q_lds, 16 * (t >> 2) + (lane & 15), lane >> 4);
   }
   pre(0, First{});
 
@@ -618,6 +627,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
     // the same dims (other rows).
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
+      if constexpr (CAPT) break;
       merge_ms(tM[u], tS[u], __shfl_xor(tM[u], 16), __shfl_xor(tS[u], 16));
       merge_ms(tM[u], tS[u], __shfl_xor(tM[u], 32), __shfl_xor(tS[u], 32));
     }
@@ -643,7 +653,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
     __syncthreads();
     // query row m: tiles t = 4 (m / 16) + kt, kt = 0..3, held by wave t % 8 in slot t / 8
     float Mf = -INFINITY, Sf = 0.f, sd = 0.f;
-    if (tid < RKV_MAX_QROWS) {
+    if (!CAPT && tid < RKV_MAX_QROWS) {
       const int qt = tid >> 4;
       if (qt < nqt16) {
 #pragma unroll
@@ -659,7 +669,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
       for (int w = 0; w < kGramWaves; ++w) sd += usc[w * kHeadDim + tid];
     }
     __syncthreads();  // the scratch is read: the tile of s rows replaces it
-    if (tid < RKV_MAX_QROWS) {
+    if (!CAPT && tid < RKV_MAX_QROWS) {
       // rows past the group's queries get (0, 0): their weights vanish
       rst_lds[2 * tid] = tid < g.qrows ? Mf : 0.f;
       rst_lds[2 * tid + 1] = tid < g.qrows ? 1.f / Sf : 0.f;
@@ -702,6 +712,21 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
             rowmean[srow + s0 + i] = (dot * inv - self) * inv_nm1;
           }
         }
+      }
+      if constexpr (CAPT) {
+        // the captured sums of the window's weights: max over the group, / alpha
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const int i = cbase + 32 * f + col;
+          if (hh == 0 && i < N) {
+            const float* a = imp_acc + (size_t)slice * g.G * g.capacity + s0 + i;
+            float best = a[0];
+            for (int gq = 1; gq < g.G; ++gq) best = fmaxf(best, a[(size_t)gq * g.capacity]);
+            importance[srow + s0 + i] = best / (float)alpha;
+          }
+        }
+        cnt[0] = cnt[1] = 0u;
+        return;
       }
       // both column fragments against the first query tile
       f32x16 accq0[2];
@@ -852,26 +877,32 @@ __global__ void redundancy_kernel(Geom g, const int32_t* __restrict__ seq_start,
 }
 
 int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q, const int32_t* seq_start,
-                const int32_t* order, float* importance, float* rowmean, int32_t* counts, void* stream) {
+                const int32_t* order, float* importance, float* rowmean, int32_t* counts, void* stream,
+                const float* imp_acc) {
   const int slices = g.L * g.batch * g.H;
   if (slices == 0) return 0;
+  if (order && imp_acc) return (int)hipErrorInvalidValue;
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid(slices), block(kGramThreads);
+#define RKV_GRAM(T, GA, CA)                                                                                   \
+  hipLaunchKernelGGL((gram_kernel<T, GA, CA>), grid, block, 0, s, g, k, obs_q, seq_start, order, imp_acc, \
+                     importance, rowmean, counts)
   if (dtype == RKV_BF16) {
     if (order)
-      hipLaunchKernelGGL((gram_kernel<bf16_t, true>), grid, block, 0, s, g, k, obs_q, seq_start, order, importance,
-                         rowmean, counts);
+      RKV_GRAM(bf16_t, true, false);
+    else if (imp_acc)
+      RKV_GRAM(bf16_t, false, true);
     else
-      hipLaunchKernelGGL((gram_kernel<bf16_t, false>), grid, block, 0, s, g, k, obs_q, seq_start, order, importance,
-                         rowmean, counts);
+      RKV_GRAM(bf16_t, false, false);
   } else {
     if (order)
-      hipLaunchKernelGGL((gram_kernel<float, true>), grid, block, 0, s, g, k, obs_q, seq_start, order, importance,
-                         rowmean, counts);
+      RKV_GRAM(float, true, false);
+    else if (imp_acc)
+      RKV_GRAM(float, false, true);
     else
-      hipLaunchKernelGGL((gram_kernel<float, false>), grid, block, 0, s, g, k, obs_q, seq_start, order, importance,
-                         rowmean, counts);
+      RKV_GRAM(float, false, false);
   }
+#undef RKV_GRAM
   return (int)hipGetLastError();
 }
 

@@ -72,8 +72,11 @@ inline Workspace carve(const rkv_params& p, void* base) {
 
 // Kernel launchers (one translation unit each). They return the hipError_t
 // of the launch as an int (0 = success).
+// With imp_acc (and no order) the importance comes from captured decode
+// attention weights instead of obs_q.
 int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q, const int32_t* seq_start,
-                const int32_t* order, float* importance, float* rowmean, int32_t* counts, void* stream);
+                const int32_t* order, float* importance, float* rowmean, int32_t* counts, void* stream,
+                const float* imp_acc = nullptr);
 int launch_redundancy(const Geom& g, const int32_t* seq_start, const int32_t* counts, const float* rowmean,
                       float* redundancy, void* stream);
 int launch_select_sampled(const Geom& g, const float* scores, const float* uniforms, const int32_t* seq_start,
@@ -85,6 +88,13 @@ int launch_sentence_penalty(const float* vectors, const int32_t* n_sent, int bat
                             float* penalty, void* stream);
 int launch_compact_ids(const Geom& g, const int32_t* keep, int32_t* ids, void* stream);
 constexpr int kSentMaxDim = 8192;
+// Decode attention with importance capture (rkv_decode.hip): query heads per
+// KV head up to kDecMaxG; dynamic LDS of decode_lds_bytes(G, n_slots) bytes.
+int launch_decode(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const void* q,
+                  const int32_t* seq_start, float* out, float* acc, void* stream);
+size_t decode_lds_bytes(int group, int n_slots);
+constexpr int kDecMaxG = 8;
+constexpr size_t kDecMaxLds = 160 * 1024 - 1024;
 // dynamic LDS of the hole-filling compaction; launches keep it within 64 KB
 size_t holefill_lds_bytes(int budget);
 constexpr size_t kHolefillMaxLds = 65536 - 2048;

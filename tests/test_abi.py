@@ -114,6 +114,10 @@ def test_bad_params_rejected_by_every_entry_point(kw, expect):
                                          check=False)
     assert st == code and ns == 384
     assert rkv.rkv_compact_holefill(p, layers(), layers(), FAKE, FAKE, FAKE, 300, stream=0, check=False) == code
+    assert rkv.rkv_decode_attention(p, layers(), layers(), FAKE, FAKE, 300, FAKE, None, stream=0, check=False) == code
+    st, ns = rkv.rkv_evict_step_captured(p, layers(), layers(), FAKE, FAKE, 384, FAKE_WS, 1 << 40, stream=0,
+                                         check=False)
+    assert st == code and ns == 384
 
 
 def test_sampled_argument_errors():
@@ -157,6 +161,41 @@ def test_sentence_argument_errors():
     for ns in (0, 383):  # below the trigger: nothing launched
         st, out = rkv.rkv_evict_step_sentences(p, layers(), layers(), FAKE, FAKE, ns, FAKE, FAKE, FAKE, 16, 64, 0.8,
                                                FAKE, FAKE_WS, need, stream=0, check=False)
+        assert st == 0 and out == ns
+
+
+def test_decode_argument_errors():
+    """Decode attention and the captured step: NULL and misaligned pointers,
+    the slot range, the group and LDS limits (nothing launched), and the
+    captured step's no-op below the trigger."""
+    p = P()
+    need = rkv.rkv_workspace_bytes(p)
+    NULL, MIS, SHAPE, UNS = (st_of(x) for x in ("RKV_ERR_NULL_ARG", "RKV_ERR_MISALIGNED", "RKV_ERR_BAD_SHAPE",
+                                                "RKV_ERR_UNSUPPORTED"))
+    dec = rkv.rkv_decode_attention
+    assert dec(p, layers(), layers(), 0, FAKE, 300, FAKE, None, stream=0, check=False) == NULL
+    assert dec(p, layers(), layers(), FAKE, 0, 300, FAKE, None, stream=0, check=False) == NULL
+    assert dec(p, layers(), layers(), FAKE, FAKE, 300, 0, None, stream=0, check=False) == NULL
+    assert dec(p, layers(), [FAKE, 0], FAKE, FAKE, 300, FAKE, None, stream=0, check=False) == NULL
+    assert dec(p, layers(), layers(), FAKE + 4, FAKE, 300, FAKE, None, stream=0, check=False) == MIS
+    assert dec(p, layers(), layers(), FAKE, FAKE, 300, FAKE + 2, None, stream=0, check=False) == MIS
+    assert dec(p, layers(), layers(), FAKE, FAKE, 300, FAKE, FAKE + 1, stream=0, check=False) == MIS
+    for ns in (0, -1, 385):
+        assert dec(p, layers(), layers(), FAKE, FAKE, ns, FAKE, None, stream=0, check=False) == SHAPE
+    # more than 8 query heads per KV head (with a 1-token window, so the params are valid)
+    assert dec(P(group=16, obs_window=1, budget=256), layers(), layers(), FAKE, FAKE, 300, FAKE, None, stream=0,
+               check=False) == UNS
+    # the weights of 8 heads over 6000 slots (192 KB) exceed the work-group's LDS
+    big = P(group=8, capacity=8000, budget=7000)
+    assert dec(big, layers(), layers(), FAKE, FAKE, 6000, FAKE, None, stream=0, check=False) == UNS
+    st, _ = rkv.rkv_evict_step_captured(p, layers(), layers(), 0, FAKE, 384, FAKE_WS, need, stream=0, check=False)
+    assert st == NULL
+    st, _ = rkv.rkv_evict_step_captured(p, layers(), layers(), FAKE + 2, FAKE, 384, FAKE_WS, need, stream=0,
+                                        check=False)
+    assert st == MIS
+    for ns in (0, 383):  # below the trigger: nothing launched
+        st, out = rkv.rkv_evict_step_captured(p, layers(), layers(), FAKE, FAKE, ns, FAKE_WS, need, stream=0,
+                                              check=False)
         assert st == 0 and out == ns
 
 
