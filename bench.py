@@ -366,6 +366,113 @@ def sweep_cpu_baseline(ds, w, budget_s: float = 20.0):
             "ms_per_step": step_s * 1e3, "cpu_seconds": one * n}
 
 
+def captured_main(args, w):
+    """Importance captured by decode attention (rkv_decode_attention with an
+    accumulator over the window, then rkv_evict_step_captured). Times, with
+    the last-level cache flushed before each: K decode-attention calls over
+    every layer without and with the accumulator (the window's last query,
+    n_slots valid slots), then K eviction steps reading the accumulator that
+    the alpha window steps filled (cache and start slots restored each time).
+    The decode kernel's roofline counts the valid K and V rows, the queries
+    and the fp32 outputs, plus the accumulator's read and write when it is on."""
+    import numpy as np
+    import torch
+
+    import synth
+    import redundancy_aware_compression_amd as rkv
+
+    cs = synth.build_cache(w, seed=args.seed)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    hip = HipEvents()
+
+    def dev_tensor(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    esz = 2 if w.dtype == "bf16" else 4
+    with torch.cuda.stream(stream):
+        K0, V0 = dev_tensor(cs.K), dev_tensor(cs.V)
+        qs = [dev_tensor(np.ascontiguousarray(cs.Q[:, :, :, t, :])) for t in range(w.obs_window)]
+        S0 = torch.from_numpy(cs.seq_start.copy()).to(dev)
+        K, V, S = K0.clone(), V0.clone(), S0.clone()
+        out = torch.empty((w.num_layers, w.batch, w.num_kv_heads * w.group, 128), dtype=torch.float32, device=dev)
+        acc = torch.zeros((w.num_layers, w.batch, w.num_kv_heads, w.group, w.capacity), dtype=torch.float32,
+                          device=dev)
+        p = rkv.make_params(w.num_layers, w.batch, w.num_kv_heads, w.group, w.capacity, w.budget, w.buffer,
+                            w.obs_window, w.beta, w.lam, w.tau, w.dtype)
+        wsb = rkv.rkv_workspace_bytes(p)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        flush_out = torch.zeros((), dtype=torch.int64, device=dev)
+        kl, vl = [K[l] for l in range(w.num_layers)], [V[l] for l in range(w.num_layers)]
+        sp = stream.cuda_stream
+        n = cs.n_slots
+
+        def flush_llc():
+            torch.sum(flush.view(torch.int64), dim=(0,), out=flush_out)
+
+        def timed(fn, k):
+            evs = [hip.create(2) for _ in range(k)]
+            for i in range(k):
+                fn(evs[i])
+            torch.cuda.synchronize()
+            ms = [hip.elapsed_ms(e[0], e[1]) for e in evs]
+            for e in evs:
+                hip.destroy(e)
+            return ms
+
+        def decode(ev, with_acc):
+            flush_llc()
+            hip.record(ev[0], sp)
+            rkv.rkv_decode_attention(p, kl, vl, qs[-1], S, n, out, acc if with_acc else None, stream=stream)
+            hip.record(ev[1], sp)
+
+        timed(lambda ev: decode(ev, False), args.warmup)
+        dec_ms = timed(lambda ev: decode(ev, False), args.steps)
+        acc.zero_()
+        dec_acc_ms = timed(lambda ev: decode(ev, True), args.steps)
+        # the window: alpha decode steps with capture, then the evictions
+        acc.zero_()
+        for t in range(w.obs_window):
+            rkv.rkv_decode_attention(p, kl, vl, qs[t], S, n - w.obs_window + 1 + t, out, acc, stream=stream)
+
+        def evict(ev):
+            K.copy_(K0)
+            V.copy_(V0)
+            S.copy_(S0)
+            flush_llc()
+            hip.record(ev[0], sp)
+            st, ns = rkv.rkv_evict_step_captured(p, kl, vl, acc, S, n, ws, wsb, stream=stream)
+            hip.record(ev[1], sp)
+            assert ns == w.budget
+
+        timed(evict, args.warmup)
+        step_ms = timed(evict, args.steps)
+    valid = int(np.minimum(cs.lengths, n).sum()) * w.num_layers * w.num_kv_heads
+    dec_bytes = 2 * valid * 128 * esz + w.num_layers * w.batch * w.num_kv_heads * w.group * 128 * (esz + 4)
+    acc_bytes = 2 * valid * w.group * 4
+    mean = lambda xs: sum(xs) / len(xs)
+    d0, d1, st_ms = mean(dec_ms), mean(dec_acc_ms), mean(step_ms)
+    out_line = {
+        "metric": METRIC, "value": 1000.0 / st_ms, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": st_ms, "us_per_step": st_ms * 1e3,
+        "us_p10": percentile(step_ms, 10) * 1e3, "us_p90": percentile(step_ms, 90) * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "importance": "captured", "slices": w.slices, "n_slots": n,
+                   "llc_flush": True, "seed": args.seed},
+        "kernels": {
+            "decode_attention": {"us": d0 * 1e3, "bytes": dec_bytes, "GB/s": dec_bytes / d0 / 1e6,
+                                 "hbm_frac": dec_bytes / d0 / 1e6 / 8000.0},
+            "decode_attention_capture": {"us": d1 * 1e3, "bytes": dec_bytes + acc_bytes,
+                                         "GB/s": (dec_bytes + acc_bytes) / d1 / 1e6,
+                                         "hbm_frac": (dec_bytes + acc_bytes) / d1 / 1e6 / 8000.0},
+        },
+    }
+    print(json.dumps(out_line), flush=True)
+
+
 def sentences_main(args, w):
     """The R-KV step with SkipKV's sentence deduction (rkv_evict_step_sentences)
     on the workload's cache and synthetic sentences (8..40 tokens, 1024-wide
@@ -558,6 +665,9 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="keep inputs warm in the last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rounds", type=int, default=0, help="sweep workloads: rounds to run (default: the recipe's)")
+    ap.add_argument("--importance", choices=["queries", "captured"], default="queries",
+                    help="queries: the step scores the observation queries (default); captured: decode attention "
+                         "captures the window's weights and the step reads them (decode attention is timed too)")
     ap.add_argument("--selection", choices=["rkv", "sampled", "sentences"], default="rkv",
                     help="rkv: the R-KV step (default); sampled: the Top-K + multinomial selection on seeded "
                          "caller scores (newest `buffer` tokens kept, top_k twice the draw) and the compaction; "
@@ -585,6 +695,8 @@ def main():
         return sampled_main(args, w)
     if args.selection == "sentences":
         return sentences_main(args, w)
+    if args.importance == "captured":
+        return captured_main(args, w)
     cs = synth.build_cache(w, seed=args.seed)
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream(device=dev)

@@ -12,16 +12,33 @@
 
 namespace rkv {
 
-constexpr int kDecThreads = 512;
-constexpr int kDecWaves = kDecThreads / 64;
+// Work-groups of 512 threads, or 256 where the weights leave room in LDS for
+// three of them per compute unit (short slices) and there are slices enough
+// for several per unit: more waves per unit then.
+constexpr int kDecMaxWaves = 8;
+constexpr size_t kDecSmallLds = 40 * 1024;
 
 // A lane holds one 16-byte chunk of a row: LPR lanes cover a row, RPI rows
-// are covered by one load instruction of the wave (fully coalesced).
+// are covered by one load instruction of the wave (fully coalesced). dot()
+// is the lane's part of q.k: bf16 pairs go to the packed dot instruction
+// unwidened (exact products, fp32 sums) and the scale comes after the row
+// sum; fp32 queries are pre-scaled.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 template <typename T>
 struct DecLanes;
 template <>
 struct DecLanes<bf16_t> {
   static constexpr int LPR = 16, EPL = 8;
+  static constexpr bool PRESCALED = false;
+  using QV = uint4;
+  __device__ static QV load_q(const char* p, float) { return *(const uint4*)p; }
+  __device__ static float d2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
+  }
+  __device__ static float dot(const uint4& k, const QV& q) {
+    return d2(k.w, q.w, d2(k.z, q.z, d2(k.y, q.y, d2(k.x, q.x, 0.f))));
+  }
   __device__ static void widen(const uint4& x, float* f) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -34,6 +51,18 @@ struct DecLanes<bf16_t> {
 template <>
 struct DecLanes<float> {
   static constexpr int LPR = 32, EPL = 4;
+  static constexpr bool PRESCALED = true;
+  using QV = float4;
+  __device__ static QV load_q(const char* p, float scale) {
+    float4 q = *(const float4*)p;
+    return make_float4(q.x * scale, q.y * scale, q.z * scale, q.w * scale);
+  }
+  __device__ static float dot(const uint4& k, const QV& q) {
+    float s = __uint_as_float(k.x) * q.x;
+    s = fmaf(__uint_as_float(k.y), q.y, s);
+    s = fmaf(__uint_as_float(k.z), q.z, s);
+    return fmaf(__uint_as_float(k.w), q.w, s);
+  }
   __device__ static void widen(const uint4& x, float* f) {
     f[0] = __uint_as_float(x.x);
     f[1] = __uint_as_float(x.y);
@@ -75,18 +104,19 @@ __device__ inline float pick(const float (&a)[G], int i) {
 // of q.k / sqrt(D) and out = sum_j w_j v_j (fp32). With acc, the weights are
 // added to acc[slice][g][s0 + j]. LDS (dynamic): the logits, then the
 // weights, as [N][G]; afterwards the waves' partial outputs [8][G][128].
-template <typename T, int G>
-__global__ __launch_bounds__(kDecThreads) void decode_kernel(Geom g, LayerPtrs k, LayerPtrs v,
+template <typename T, int G, int NT>
+__global__ __launch_bounds__(NT) void decode_kernel(Geom g, LayerPtrs k, LayerPtrs v,
                                                              const void* __restrict__ q,
                                                              const int32_t* __restrict__ seq_start,
                                                              float* __restrict__ out, float* __restrict__ acc) {
   using DL = DecLanes<T>;
   constexpr int LPR = DL::LPR, EPL = DL::EPL, RPI = 64 / LPR;
   constexpr int RB = kHeadDim * (int)sizeof(T);
-  constexpr int U = G * EPL <= 32 ? 8 : 4;  // row loads per lane in flight (fewer with more query registers)
-  constexpr int STEP = kDecWaves * RPI * U;  // rows per round of the work-group
+  constexpr int NW = NT / 64;
+  constexpr int U = 4;  // row loads per lane per round (two rounds in flight)
+  constexpr int STEP = NW * RPI * U;  // rows per round of the work-group
   extern __shared__ __align__(16) float lw[];
-  __shared__ float red_m[kDecWaves][G], red_s[kDecWaves][G];
+  __shared__ float red_m[NW][G], red_s[NW][G];
 
   const int slice = blockIdx.x;
   int l, b, h, s0, N;
@@ -95,54 +125,56 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(Geom g, LayerPtrs k
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane % LPR, rr = lane / LPR;
   float* o_out = out + (size_t)slice * G * kHeadDim;
   if (N == 0) {
-    for (int e = tid; e < G * kHeadDim; e += kDecThreads) o_out[e] = 0.f;
+    for (int e = tid; e < G * kHeadDim; e += NT) o_out[e] = 0.f;
     return;
   }
   const char* kb = row_ptr<T>(k.p[l], g, b, h, s0);
   const char* vb = row_ptr<T>(v.p[l], g, b, h, s0);
 
-  // the lane's chunk of each query row, scaled so that logits are in log2 units
+  // the lane's chunk of each query row; logits are in log2 units
   const float qs = 1.4426950408889634f / sqrtf((float)kHeadDim);
-  float qf[G][EPL];
+  typename DL::QV qv[G];
   {
     const char* qb = (const char*)q + (size_t)slice * G * RB;
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-      DL::widen(*(const uint4*)(qb + gi * RB + c * 16), qf[gi]);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) qf[gi][e] *= qs;
-    }
+    for (int gi = 0; gi < G; ++gi) qv[gi] = DL::load_q(qb + gi * RB + c * 16, qs);
   }
+
+  // Rounds of U loads per lane, software-pipelined: the next round is issued
+  // (rows clamped into the slice) before the current one is used, and the
+  // K pass's last prefetch is the V pass's first round, so those loads fly
+  // across the softmax below.
+  auto load_round = [&](uint4(&x)[U], const char* base, int j0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = min(j0 + u * RPI + rr, N - 1);
+      x[u] = *(const uint4*)(base + (size_t)row * RB + c * 16);
+    }
+  };
+  const int jstart = wave * RPI * U;
+  uint4 xa[U], xb[U];
+  load_round(xa, kb, jstart);
 
   // ---- logits: lane c < G of each row stores query c's logit and keeps its max
   float mrun = -INFINITY;
-  for (int j0 = wave * RPI * U; j0 < N; j0 += STEP) {
-    uint4 x[U];
+  for (int j0 = jstart; j0 < N; j0 += STEP) {
+    const int jn = j0 + STEP;
+    load_round(xb, jn < N ? kb : vb, jn < N ? jn : jstart);
+    __builtin_amdgcn_sched_barrier(0);  // the next round's loads go out before this round's work
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int row = min(j0 + u * RPI + rr, N - 1);  // rows past the slice re-read its last row, unused
-      x[u] = *(const uint4*)(kb + (size_t)row * RB + c * 16);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // all loads of the round before their uses
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float kf[EPL];
-      DL::widen(x[u], kf);
       float part[G];
 #pragma unroll
-      for (int gi = 0; gi < G; ++gi) {
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) s = fmaf(qf[gi][e], kf[e], s);
-        part[gi] = row_sum<LPR>(s);
-      }
+      for (int gi = 0; gi < G; ++gi) part[gi] = row_sum<LPR>(DL::dot(xa[u], qv[gi]));
       const int row = j0 + u * RPI + rr;
       if (c < G && row < N) {
-        const float lg = pick<G>(part, c);
+        const float lg = DL::PRESCALED ? pick<G>(part, c) : pick<G>(part, c) * qs;
         lw[row * G + c] = lg;
         mrun = fmaxf(mrun, lg);
       }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) xa[u] = xb[u];
   }
 #pragma unroll
   for (int o = LPR; o < 64; o <<= 1) mrun = fmaxf(mrun, __shfl_xor(mrun, o));
@@ -153,14 +185,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(Geom g, LayerPtrs k
   for (int gi = 0; gi < G; ++gi) {
     m[gi] = red_m[0][gi];
 #pragma unroll
-    for (int w = 1; w < kDecWaves; ++w) m[gi] = fmaxf(m[gi], red_m[w][gi]);
+    for (int w = 1; w < NW; ++w) m[gi] = fmaxf(m[gi], red_m[w][gi]);
   }
 
   // ---- weights (unnormalised) and their sums
   float ssum[G];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) ssum[gi] = 0.f;
-  for (int e = tid; e < N * G; e += kDecThreads) {
+  for (int e = tid; e < N * G; e += NT) {
     const int gi = e % G;
     const float p = exp2f(lw[e] - pick<G>(m, gi));
     lw[e] = p;
@@ -178,23 +210,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(Geom g, LayerPtrs k
   for (int gi = 0; gi < G; ++gi) {
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) s += red_s[w][gi];
+    for (int w = 0; w < NW; ++w) s += red_s[w][gi];
     inv[gi] = 1.f / s;
   }
 
-  // ---- output: o[g] = sum_j p_j v_j over the lane's rows and dims
+  // ---- output: o[g] = sum_j p_j v_j over the lane's rows and dims (xa holds
+  // the first round of V)
   float o[G][EPL];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[gi][e] = 0.f;
-  for (int j0 = wave * RPI * U; j0 < N; j0 += STEP) {
-    uint4 x[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int row = min(j0 + u * RPI + rr, N - 1);
-      x[u] = *(const uint4*)(vb + (size_t)row * RB + c * 16);
-    }
+  for (int j0 = jstart; j0 < N; j0 += STEP) {
+    load_round(xb, vb, j0 + STEP);  // past the slice: its last row again, unused
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -202,7 +230,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(Geom g, LayerPtrs k
       const bool ok = row < N;
       const int rc = ok ? row : N - 1;  // in-bounds index for rows past the slice, weight 0
       float vf[EPL];
-      DL::widen(x[u], vf);
+      DL::widen(xa[u], vf);
 #pragma unroll
       for (int gi = 0; gi < G; ++gi) {
         const float p = ok ? lw[rc * G + gi] : 0.f;
@@ -210,14 +238,31 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(Geom g, LayerPtrs k
         for (int e = 0; e < EPL; ++e) o[gi][e] = fmaf(p, vf[e], o[gi][e]);
       }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) xa[u] = xb[u];
   }
 
   // ---- capture: acc[g][j] += w_gj
   if (acc) {
-    float* ab = acc + (size_t)slice * G * g.capacity + s0;
+    constexpr int CU = 4;  // accumulator reads in flight per thread
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi)
-      for (int j = tid; j < N; j += kDecThreads) ab[(size_t)gi * g.capacity + j] += lw[j * G + gi] * inv[gi];
+    for (int gi = 0; gi < G; ++gi) {
+      float* ab = acc + ((size_t)slice * G + gi) * g.capacity + s0;
+      for (int j0 = tid; j0 < N; j0 += CU * NT) {
+        float a[CU];
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+          const int j = j0 + u * NT;
+          a[u] = j < N ? ab[j] : 0.f;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+          const int j = j0 + u * NT;
+          if (j < N) ab[j] = fmaf(lw[j * G + gi], inv[gi], a[u]);
+        }
+      }
+    }
   }
 
   // ---- combine the rows of the wave, then the waves
@@ -235,31 +280,39 @@ __global__ __launch_bounds__(kDecThreads) void decode_kernel(Geom g, LayerPtrs k
       for (int e = 0; e < EPL; ++e) lw[(wave * G + gi) * kHeadDim + c * EPL + e] = o[gi][e];
   }
   __syncthreads();
-  for (int e = tid; e < G * kHeadDim; e += kDecThreads) {
+  for (int e = tid; e < G * kHeadDim; e += NT) {
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) s += lw[w * G * kHeadDim + e];
+    for (int w = 0; w < NW; ++w) s += lw[w * G * kHeadDim + e];
     o_out[e] = s * pick<G>(inv, e / kHeadDim);
   }
 }
 
 size_t decode_lds_bytes(int group, int n_slots) {
-  const int rows = n_slots > kDecWaves * kHeadDim ? n_slots : kDecWaves * kHeadDim;
+  const int rows = n_slots > kDecMaxWaves * kHeadDim ? n_slots : kDecMaxWaves * kHeadDim;
   return (size_t)group * rows * 4;
+}
+
+template <typename T, int G, int NT>
+static int launch_decode_nt(const Geom& g, const LayerPtrs& k, const LayerPtrs& v, const void* q,
+                            const int32_t* seq_start, float* out, float* acc, hipStream_t s, size_t lds) {
+  if (lds > 65536) {
+    const int err = (int)hipFuncSetAttribute((const void*)decode_kernel<T, G, NT>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err) return err;
+  }
+  hipLaunchKernelGGL((decode_kernel<T, G, NT>), dim3(g.L * g.batch * g.H), dim3(NT), lds, s, g, k, v, q,
+                     seq_start, out, acc);
+  return (int)hipGetLastError();
 }
 
 template <typename T, int G>
 static int launch_decode_g(const Geom& g, const LayerPtrs& k, const LayerPtrs& v, const void* q,
                            const int32_t* seq_start, float* out, float* acc, hipStream_t s) {
   const size_t lds = decode_lds_bytes(G, g.n_slots);
-  if (lds > 65536) {
-    const int err = (int)hipFuncSetAttribute((const void*)decode_kernel<T, G>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err) return err;
-  }
-  hipLaunchKernelGGL((decode_kernel<T, G>), dim3(g.L * g.batch * g.H), dim3(kDecThreads), lds, s, g, k, v, q,
-                     seq_start, out, acc);
-  return (int)hipGetLastError();
+  const bool small = lds <= kDecSmallLds && g.L * g.batch * g.H >= 4 * kCUs;
+  return small ? launch_decode_nt<T, G, 256>(g, k, v, q, seq_start, out, acc, s, lds)
+               : launch_decode_nt<T, G, 512>(g, k, v, q, seq_start, out, acc, s, lds);
 }
 
 template <typename T>

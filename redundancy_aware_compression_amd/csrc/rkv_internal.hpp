@@ -20,6 +20,7 @@ constexpr int kRowBlock = 64;    // Gram rows (newer tokens) per LDS stage; colu
 constexpr int kGramWaves = 8;    // waves per Gram work-group (one slice per work-group)
 constexpr int kGroupBlocks = kGramWaves;  // 64-column blocks per column group
 constexpr int kXcds = 8;         // MI355X accelerator complex dies
+constexpr int kCUs = 256;        // MI355X compute units
 
 // Geometry and method parameters common to every kernel.
 struct Geom {

@@ -7,8 +7,9 @@ attention, importance scoring and eviction as the way to cut compression's
 cost (Q&A part 2, cause 4).
 
 - Output of one decode step (the window's last query) against
-  oracle.decode_attention, on bf16 and fp32 caches, group sizes 1 to 8, a
-  ragged batch and a slice long enough for more than 64 KiB of weights.
+  oracle.decode_attention, on bf16 and fp32 caches, group sizes 1 to 8,
+  ragged batches (one with 8192 slices, which takes the 256-thread
+  work-groups) and a slice long enough for more than 64 KiB of weights.
 - Edge cases: a sequence with no valid slot (output 0, accumulator
   untouched) and one whose only key is its own (output = its value, exactly).
 - The alpha window steps with capture: max over the group of the sums / alpha
@@ -46,8 +47,11 @@ WORKLOADS = {
     "single_f32": synth.WORKLOADS["single_f32"],
     "small_long": synth.small("small_long", 108, num_layers=1, batch=1, num_kv_heads=2, group=4, budget=5600),
     "llama8b_b1": synth.WORKLOADS["llama8b_b1"],
+    # 8192 slices of at most 1152 slots: the 256-thread work-groups
+    "llama8b_b32_ragged": synth.WORKLOADS["llama8b_b32_ragged"],
 }
-SAMPLED = {"llama8b_b1": [(0, 0, 0), (7, 0, 5), (19, 0, 2), (31, 0, 7)]}
+SAMPLED = {"llama8b_b1": [(0, 0, 0), (7, 0, 5), (19, 0, 2), (31, 0, 7)],
+           "llama8b_b32_ragged": [(0, 0, 0), (5, 17, 3), (12, 3, 1), (31, 31, 7), (20, 9, 4)]}
 
 
 def slices_of(w, name):
