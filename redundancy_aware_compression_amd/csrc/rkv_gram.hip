@@ -465,7 +465,6 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
 #pragma unroll
   for (int e = 0; e < 16; ++e) run[e] = 0.f;
   float tM[2] = {-INFINITY, -INFINITY}, tS[2] = {0.f, 0.f};  // logit tiles wave and wave + 8
-  typename TL::F qtile[2];  // their query fragments (group 0 only), from LDS after the first barrier
   int pg = 0, pbi = 0;  // the pre-pass cursor: block pbi of group pg
   // row block blk keeps its norms in nrm_all once group 0 has seen it
   auto cached = [&](int blk) { return (blk + 1) * kRowBlock <= S::NCACHE; };
@@ -508,7 +507,9 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
         typename TL::F ka;
         TL::load(ka, st, 16 * kt + (lane & 15), lane >> 4);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        TL::mma(acc, ka, qtile[u]);
+        typename TL::F qf;  // the query rows' fragment, read from LDS (fewer live registers than keeping it)
+        TL::load(qf, q_lds, 16 * qt + (lane & 15), lane >> 4);
+        TL::mma(acc, ka, qf);
         const uint32_t m = 16u * qt + (uint32_t)(lane & 15);
         const int pos = N - alpha + (int)(m - ((m * magic) >> 16) * (uint32_t)alpha);  // query's token
         float xs[4], mx = -INFINITY;
@@ -543,11 +544,6 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   else
     wait_later_blocks<S::PER>(pro_n - 1);
   __syncthreads();
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int t = wave + 8 * u;
-    if (!CAPT && t < 4 * nqt16) TL::load(qtile[u], q_lds, 16 * (t >> 2) + (lane & 15), lane >> 4);
-  }
   pre(0, First{});
 
   Frag<T> bf[2];  // this group's column keys of the wave: fragment f holds columns cbase + 32 f + (0..31)
@@ -591,6 +587,44 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
         }
       }
       uint32_t bits[2] = {0u, 0u};  // sign bits of the block's 32 rows per column fragment
+      if (!GATHER && sizeof(T) == 2 && __builtin_expect(!diag, 1)) {
+        // Both 32-row halves' products first, then the first half's epilogue
+        // placed between the second half's 16 MFMAs (4 VALU after each): the
+        // epilogue runs in the matrix units' shadow. (With GATHER, or fp32
+        // keys, the extra accumulators would not fit in registers.)
+        float nj0[16], nj1[16];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const float4 v0 = *(const float4*)&ns[8 * a + 4 * hh];
+          const float4 v1 = *(const float4*)&ns[32 + 8 * a + 4 * hh];
+          nj0[4 * a + 0] = fabsf(v0.x);
+          nj0[4 * a + 1] = fabsf(v0.y);
+          nj0[4 * a + 2] = fabsf(v0.z);
+          nj0[4 * a + 3] = fabsf(v0.w);
+          nj1[4 * a + 0] = fabsf(v1.x);
+          nj1[4 * a + 1] = fabsf(v1.y);
+          nj1[4 * a + 2] = fabsf(v1.z);
+          nj1[4 * a + 3] = fabsf(v1.w);
+        }
+        Frag<T> af0, af1;
+        frag_from_stage(af0, st, col, hh);
+        frag_from_stage(af1, st, 32 + col, hh);
+        f32x16 a00 = {}, a01 = {}, a10 = {}, a11 = {};
+        mma_frag(a00, af0, bf[0]);
+        mma_frag(a01, af0, bf[1]);
+        mma_frag(a10, af1, bf[0]);
+        mma_frag(a11, af1, bf[1]);
+        bits[0] = sign_bits(a00, tn[0], nj0, 0u);
+        bits[1] = sign_bits(a01, tn[1], nj0, 0u);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // the first half's MFMAs
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one of the second half's
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four epilogue VALU
+        }
+        bits[0] = sign_bits(a10, tn[0], nj1, bits[0]);
+        bits[1] = sign_bits(a11, tn[1], nj1, bits[1]);
+      } else
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
         Frag<T> af;
