@@ -170,7 +170,20 @@ def cpu_baseline(cs, budget_s: float = 20.0):
     return {"value": 1.0 / step_s, "unit": "steps/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} of {len(evicting)} evicting slices (score, select, K/V gather), one slice per task "
                       f"on {cores} threads; step time extrapolated from the sample's wall time",
-            "ms_per_step": step_s * 1e3, "cpu_seconds": one * n}
+            "ms_per_step": step_s * 1e3, "cpu_seconds": one * n,
+            "us_per_slice_1core": one * 1e6, "ms_per_step_1core": one * len(evicting) * 1e3,
+            "nproc": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def kernel_table(w, ev_lens, moved, means, holefill=False):
@@ -196,8 +209,10 @@ def kernel_table(w, ev_lens, moved, means, holefill=False):
         "compact": {"us": means[2] * 1e3, "bound": "hbm", "bytes": k5_bytes, "moved_rows": moved,
                     "achieved": k5_bytes / (means[2] * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"},
     }
-    for k in kernels.values():
+    for name, k in kernels.items():
         k["frac"] = k["achieved"] / k["peak"]
+        if not (holefill and name == "compact"):  # rocprofv3 FETCH_SIZE + WRITE_SIZE, when summarised
+            k["traffic"] = measured_traffic(name, w.name)
     dom = max(["gram", "compact"], key=lambda k: kernels[k]["us"])
     if holefill:
         kernels["compact"]["kernel"] = "holefill_kernel"
@@ -792,11 +807,21 @@ def main():
         for i in range(args.steps):
             staged_step(sevs[i])
         torch.cuda.synchronize()
+        # warm pass: the same steps with the inputs left in the last-level cache
+        wevs = []
+        if not args.no_flush:
+            args.no_flush = True
+            wevs = [hip.create(2) for _ in range(args.steps)]
+            for i in range(args.steps):
+                plain_step(wevs[i])
+            torch.cuda.synchronize()
+            args.no_flush = False
 
     step_ms = [hip.elapsed_ms(e[0], e[1]) for e in evs]
     staged_ms = [hip.elapsed_ms(e[0], e[3]) for e in sevs]
     stage_ms = [[hip.elapsed_ms(e[s], e[s + 1]) for e in sevs] for s in range(3)]
-    for e in evs + sevs + [warm]:
+    warm_ms = [hip.elapsed_ms(e[0], e[1]) for e in wevs]
+    for e in evs + sevs + wevs + [warm]:
         hip.destroy(e)
     mean_ms = sum(step_ms) / len(step_ms)
 
@@ -812,6 +837,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": mean_ms,
         "us_per_step": mean_ms * 1e3,
+        "us_median": percentile(step_ms, 50) * 1e3,
         "us_p10": percentile(step_ms, 10) * 1e3,
         "us_p90": percentile(step_ms, 90) * 1e3,
         "us_per_step_with_kernel_marks": sum(staged_ms) / len(staged_ms) * 1e3,
@@ -826,9 +852,14 @@ def main():
                    "slices": w.slices, "n_slots": cs.n_slots, "llc_flush": not args.no_flush, "seed": args.seed,
                    "layout": args.layout},
         "wall_ms_per_iteration": wall * 1e3 / args.steps,
+        "moved_rows": moved,
         "kernels": kernels,
         "roofline": roofline,
     }
+    if warm_ms:
+        out["warm"] = {"us_per_step": sum(warm_ms) / len(warm_ms) * 1e3, "us_median": percentile(warm_ms, 50) * 1e3,
+                       "us_p10": percentile(warm_ms, 10) * 1e3, "us_p90": percentile(warm_ms, 90) * 1e3,
+                       "note": "inputs left in the last-level cache (no flush between steps)"}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cs)
     print(json.dumps(out), flush=True)
