@@ -46,6 +46,9 @@ WORKLOADS = {
                              obs_window=64),
     "single_f32": synth.WORKLOADS["single_f32"],
     "small_long": synth.small("small_long", 108, num_layers=1, batch=1, num_kv_heads=2, group=4, budget=5600),
+    # the largest capacity (16384 slots); group 2 keeps the weights at 128 KiB of LDS
+    "max_capacity_g2": synth.small("max_capacity_g2", 123, num_layers=1, batch=1, num_kv_heads=1, group=2,
+                                   budget=16384 - 128),
     "llama8b_b1": synth.WORKLOADS["llama8b_b1"],
     # 8192 slices of at most 1152 slots: the 256-thread work-groups
     "llama8b_b32_ragged": synth.WORKLOADS["llama8b_b32_ragged"],

@@ -36,6 +36,10 @@ SMALL = {
     # more tokens than the scoring kernel keeps norms of in LDS: the later
     # column groups recompute the newest blocks' norms
     "small_long": synth.small("small_long", 108, num_layers=1, batch=1, num_kv_heads=2, group=4, budget=5600),
+    # the largest capacity the library takes (RKV_MAX_CAPACITY = 16384 slots): 32 column groups,
+    # norms past the scoring kernel's LDS cache, the selection's full key array
+    "max_capacity": synth.small("max_capacity", 122, num_layers=1, batch=1, num_kv_heads=1, group=4,
+                                budget=16384 - 128),
 }
 
 # (workload, sampled (layer, sequence, head) slices)
