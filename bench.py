@@ -62,12 +62,9 @@ def kernel_source_digest(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch of `kernel` on `workload` from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (calibrated against a copy of
-    known size), or None when there is no summary or it was taken on other
-    kernel sources."""
-    path = os.path.join(PROFILES, f"{kernel}_{workload}_hbm_traffic.md")
+def _profile_fields(kernel: str, path: str):
+    """The `- key: value` fields of a committed profile summary, or None when
+    there is none or it was taken on other kernel sources."""
     if not os.path.exists(path):
         return None
     fields = {}
@@ -78,8 +75,28 @@ def measured_traffic(kernel: str, workload: str):
                 fields[k.strip().strip("`")] = v.strip().strip("`")
     if fields.get("source_digest") != kernel_source_digest(kernel):
         return None
+    return fields
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (calibrated against a copy of
+    known size), or None when there is no summary or it was taken on other
+    kernel sources."""
+    fields = _profile_fields(kernel, os.path.join(PROFILES, f"{kernel}_{workload}_hbm_traffic.md"))
     try:
-        return int(fields["traffic_bytes_per_launch"])
+        return int(fields["traffic_bytes_per_launch"]) if fields else None
+    except (KeyError, ValueError):
+        return None
+
+
+def measured_mfma_busy(workload: str):
+    """The scoring kernel's MFMA busy fraction on `workload` from the committed
+    rocprofv3 summary (SQ_VALU_MFMA_BUSY_CYCLES over GUI-active cycles of all
+    SIMDs), or None as for measured_traffic."""
+    fields = _profile_fields("gram", os.path.join(PROFILES, f"gram_{workload}_mfma_counters.md"))
+    try:
+        return float(fields["mfma_busy_fraction"]) if fields else None
     except (KeyError, ValueError):
         return None
 
@@ -213,6 +230,8 @@ def kernel_table(w, ev_lens, moved, means, holefill=False):
         k["frac"] = k["achieved"] / k["peak"]
         if not (holefill and name == "compact"):  # rocprofv3 FETCH_SIZE + WRITE_SIZE, when summarised
             k["traffic"] = measured_traffic(name, w.name)
+    if not holefill:  # the same fraction from counters: MFMA busy cycles over all SIMDs' cycles
+        kernels["gram"]["frac_counters"] = measured_mfma_busy(w.name)
     dom = max(["gram", "compact"], key=lambda k: kernels[k]["us"])
     if holefill:
         kernels["compact"]["kernel"] = "holefill_kernel"
@@ -221,6 +240,8 @@ def kernel_table(w, ev_lens, moved, means, holefill=False):
     roofline = {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"], "peak": dk["peak"],
                 "unit": dk["unit"], "frac": dk["frac"],
                 "traffic": measured_traffic(dom, w.name) if not (holefill and dom == "compact") else None}
+    if dk.get("frac_counters") is not None:
+        roofline["frac_counters"] = dk["frac_counters"]
     return kernels, roofline
 
 
