@@ -509,6 +509,81 @@ def captured_main(args, w):
     print(json.dumps(out_line), flush=True)
 
 
+def peaks_main(args):
+    """Measured peaks of the chip, for context beside the published ones the
+    rooflines use: bf16 MFMA flops (four independent 32x32x16 chains per wave,
+    2048 work-groups of 4 waves), HBM read (4 GiB, 5x the last-level cache and
+    more) and HBM copy (2 GiB to 2 GiB), each the best of --steps launches
+    between HIP events after one warm-up."""
+    import torch
+
+    from redundancy_aware_compression_amd import build as rkv_build
+
+    lib = ctypes.CDLL(rkv_build.PEAKS_LIB_PATH)
+    lib.rkv_peak_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.rkv_peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    lib.rkv_peak_hbm_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                      ctypes.c_void_p]
+    tpb = lib.rkv_peak_threads_per_block()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    hip = HipEvents()
+    blocks, iters = 2048, 20000
+    hbm_blocks = 4096
+    read_bytes, copy_bytes = 4 << 30, 2 << 30
+    reps = max(3, min(args.steps, 10))
+
+    def best_ms(fn):
+        fn()  # warm-up
+        evs = [hip.create(2) for _ in range(reps)]
+        for e in evs:
+            hip.record(e[0], stream.cuda_stream)
+            fn()
+            hip.record(e[1], stream.cuda_stream)
+        torch.cuda.synchronize()
+        ms = min(hip.elapsed_ms(e[0], e[1]) for e in evs)
+        for e in evs:
+            hip.destroy(e)
+        return ms
+
+    with torch.cuda.stream(stream):
+        out = torch.empty(blocks * tpb, dtype=torch.float32, device=dev)
+        buf = torch.ones(read_bytes, dtype=torch.uint8, device=dev)
+        red = torch.empty(hbm_blocks, dtype=torch.int32, device=dev)
+        dst = torch.empty(copy_bytes, dtype=torch.uint8, device=dev)
+        sp = ctypes.c_void_p(stream.cuda_stream)
+
+        def check(rc, what):
+            if rc != 0:
+                raise RuntimeError(f"{what}: hipError {rc}")
+
+        mfma_ms = best_ms(lambda: check(lib.rkv_peak_mfma_bf16(blocks, iters, out.data_ptr(), sp), "mfma"))
+        read_ms = best_ms(lambda: check(lib.rkv_peak_hbm_read(buf.data_ptr(), read_bytes, hbm_blocks, red.data_ptr(),
+                                                              sp), "read"))
+        copy_ms = best_ms(lambda: check(lib.rkv_peak_hbm_copy(buf.data_ptr(), dst.data_ptr(), copy_bytes, hbm_blocks,
+                                                              sp), "copy"))
+    flops = blocks * (tpb // 64) * iters * 4 * 32768
+    line = {
+        "peaks": {
+            "mfma_bf16_tflops": flops / (mfma_ms * 1e-3) / 1e12,
+            "hbm_read_gbs": read_bytes / (read_ms * 1e-3) / 1e9,
+            "hbm_copy_gbs": 2 * copy_bytes / (copy_ms * 1e-3) / 1e9,
+        },
+        "published": {"mfma_bf16_tflops": BF16_PEAK_TFLOPS, "hbm_gbs": HBM_PEAK_GBS},
+        "config": {"mfma": f"{blocks} work-groups x {tpb // 64} waves x {iters} rounds x 4 MFMA 32x32x16 bf16",
+                   "hbm": f"{hbm_blocks} work-groups x {tpb} threads over 32 KiB tiles, 8 non-temporal 16-byte loads "
+                          "in flight per thread",
+                   "hbm_read_bytes": read_bytes, "hbm_copy_bytes": copy_bytes, "best_of": reps},
+    }
+    line["fraction_of_published"] = {
+        "mfma_bf16": line["peaks"]["mfma_bf16_tflops"] / BF16_PEAK_TFLOPS,
+        "hbm_read": line["peaks"]["hbm_read_gbs"] / HBM_PEAK_GBS,
+        "hbm_copy": line["peaks"]["hbm_copy_gbs"] / HBM_PEAK_GBS,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def sentences_main(args, w):
     """The R-KV step with SkipKV's sentence deduction (rkv_evict_step_sentences)
     on the workload's cache and synthetic sentences (8..40 tokens, 1024-wide
@@ -701,6 +776,9 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="keep inputs warm in the last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rounds", type=int, default=0, help="sweep workloads: rounds to run (default: the recipe's)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure the chip's bf16 MFMA issue rate and HBM read / copy bandwidth with the peak "
+                         "microbenchmarks (librkv_peaks.so) instead of the eviction step")
     ap.add_argument("--importance", choices=["queries", "captured"], default="queries",
                     help="queries: the step scores the observation queries (default); captured: decode attention "
                          "captures the window's weights and the step reads them (decode attention is timed too)")
@@ -724,6 +802,8 @@ def main():
     import synth
     import redundancy_aware_compression_amd as rkv
 
+    if args.peaks:
+        return peaks_main(args)
     w = synth.WORKLOADS[args.workload]
     if w.name in SWEEP_WORKLOADS:
         return sweep_main(args, w)

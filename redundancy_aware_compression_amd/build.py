@@ -1,4 +1,5 @@
-"""Builds librkv.so (the gfx950 HIP kernels and the C-ABI host layer) in place.
+"""Builds librkv.so (the gfx950 HIP kernels and the C-ABI host layer) and
+librkv_peaks.so (peak microbenchmarks, measurement only) in place.
 
     python -m redundancy_aware_compression_amd.build
 
@@ -17,6 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "librkv.so")
+PEAKS_SRC = os.path.join(PKG, "peaks", "rkv_peaks.hip")
+PEAKS_LIB_PATH = os.path.join(PKG, "librkv_peaks.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # MFMA accumulators in VGPRs (no accumulator-register copies before the epilogues)
@@ -54,7 +57,22 @@ def build(verbose: bool = False) -> str:
         if r.returncode != 0:
             raise RuntimeError(f"link failed:\n{r.stderr}")
         os.replace(tmp_so, LIB_PATH)
+    build_peaks(verbose)
     return LIB_PATH
+
+
+def build_peaks(verbose: bool = False) -> str:
+    """librkv_peaks.so: the peak microbenchmarks (measurement only)."""
+    tmp_so = PEAKS_LIB_PATH + ".tmp"
+    cmd = [HIPCC] + COMMON_FLAGS + DEVICE_FLAGS + ["-shared", PEAKS_SRC, "-o", tmp_so]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        err = "\n".join(line for line in r.stderr.splitlines() if "packed-fp32-ops" not in line)
+        raise RuntimeError(f"hipcc failed on {PEAKS_SRC}:\n{err}")
+    os.replace(tmp_so, PEAKS_LIB_PATH)
+    return PEAKS_LIB_PATH
 
 
 if __name__ == "__main__":

@@ -289,3 +289,25 @@ def test_no_launch_paths_return_ok():
 def test_python_raises_on_error():
     with pytest.raises(rkv.RkvError, match="RKV_ERR_BAD_PARAM"):
         rkv.rkv_select(P(lam=2.0), FAKE, FAKE, FAKE, 300, FAKE, stream=0)
+
+
+def test_peaks_library_exports_its_header():
+    """librkv_peaks.so (the peak microbenchmarks) exports what include/rkv_peaks.h
+    declares; its argument checks run on the host (nothing is launched)."""
+    from redundancy_aware_compression_amd import build as rkv_build
+
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "rkv_peaks.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(rkv_peak_[a-z_0-9]+)\s*\(", text)))
+    assert {"rkv_peak_mfma_bf16", "rkv_peak_hbm_read", "rkv_peak_hbm_copy"} <= set(names)
+    lib = ctypes.CDLL(rkv_build.PEAKS_LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    lib.rkv_peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    lib.rkv_peak_hbm_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                      ctypes.c_void_p]
+    lib.rkv_peak_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.rkv_peak_hbm_read(FAKE, 100, 4, FAKE, None) != 0  # not a multiple of 16
+    assert lib.rkv_peak_hbm_copy(FAKE + 8, FAKE, 4096, 4, None) != 0  # misaligned
+    assert lib.rkv_peak_mfma_bf16(0, 10, FAKE, None) != 0  # no work-groups
+    assert lib.rkv_peak_threads_per_block() == 256
