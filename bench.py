@@ -52,13 +52,15 @@ KERNEL_SOURCES = {
 
 
 def kernel_source_digest(kernel: str) -> str:
-    """Short digest of the sources and build script a kernel is compiled from."""
+    """Short digest of the sources a kernel is compiled from and the compiler
+    flags of librkv.so."""
+    from redundancy_aware_compression_amd import build as rkv_build
+
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
-    with open(os.path.join(ROOT, "redundancy_aware_compression_amd", "build.py"), "rb") as fh:
-        h.update(fh.read())
+    h.update(repr((rkv_build.COMMON_FLAGS[:3], rkv_build.DEVICE_FLAGS)).encode())
     return h.hexdigest()[:16]
 
 
