@@ -146,13 +146,28 @@ __global__ __launch_bounds__(kHoleThreads) void holefill_kernel(Geom g, LayerPtr
 
   // 1. the keep list (virtual slots, ascending after the leading -1) and the old order
   int nlead = 0, nstay = 0;
-  for (int j = tid; j < B; j += kHoleThreads) {
-    const int kv = krow[j], o = orow[j];
-    const bool valid = kv >= 0 && kv < g.n_slots;
-    kl[j] = valid ? (uint16_t)kv : (uint16_t)0xFFFF;
-    ol[j] = (uint16_t)(o >= 0 && o < B ? o : 0xFFFF);
-    nlead += kv < 0 ? 1 : 0;
-    nstay += valid && kv < B ? 1 : 0;
+  constexpr int kLd = 8;  // keep and order entries per thread per round, loaded before use
+  for (int j0 = tid; j0 < B; j0 += kLd * kHoleThreads) {
+    int kvs[kLd], os[kLd];
+#pragma unroll
+    for (int u = 0; u < kLd; ++u) {
+      const int j = min(j0 + u * kHoleThreads, B - 1);
+      kvs[u] = krow[j];
+      os[u] = orow[j];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kLd; ++u) {
+      const int j = j0 + u * kHoleThreads;
+      if (j < B) {
+        const int kv = kvs[u], o = os[u];
+        const bool valid = kv >= 0 && kv < g.n_slots;
+        kl[j] = valid ? (uint16_t)kv : (uint16_t)0xFFFF;
+        ol[j] = (uint16_t)(o >= 0 && o < B ? o : 0xFFFF);
+        nlead += kv < 0 ? 1 : 0;
+        nstay += valid && kv < B ? 1 : 0;
+      }
+    }
   }
   for (int w = tid; w < nwords; w += kHoleThreads) used[w] = 0u;
   int both;  // the two counts in one reduction (each below 2^16)
