@@ -28,32 +28,33 @@ __device__ inline uint32_t order_key(float z) {
 }
 
 // Exact k-th largest of keys[0 .. n) (1 <= k <= n) by four 8-bit radix
-// passes over an LDS histogram: T is that key and `need` the number of keys
+// passes over LDS histograms: T is that key and `need` the number of keys
 // equal to T among the top k. Every thread of the work-group takes part and
-// receives both.
-__device__ inline void radix_kth(const uint32_t* keys, int n, int k, int* hist, int* sel_digit, int* sel_above,
-                                 uint32_t& T, int& need) {
+// receives both. hist holds two 256-bin histograms: while one pass's digit is
+// found, the other is cleared for the next pass, so each pass needs two
+// barriers. sel[0], sel[1]: the pass's digit and the keys above it. Every
+// read of keys is done when this returns.
+__device__ inline void radix_kth(const uint32_t* keys, int n, int k, int* hist, int* sel, uint32_t& T, int& need) {
   const int tid = threadIdx.x, nt = blockDim.x;
   uint32_t prefix = 0;
   need = k;
+  for (int d = tid; d < 256; d += nt) hist[d] = 0;
+  __syncthreads();
 #pragma unroll 1
   for (int pass = 0; pass < 4; ++pass) {
+    int* h = hist + (pass & 1) * 256;
+    int* hn = hist + ((pass + 1) & 1) * 256;
     const int shift = 24 - 8 * pass;
     const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for (int d = tid; d < 256; d += nt) hist[d] = 0;
-    if (tid == 0) {
-      *sel_digit = 0;
-      *sel_above = 0;
-    }
-    __syncthreads();
     for (int i = tid; i < n; i += nt) {
       const uint32_t key = keys[i];
-      if ((key & hi_mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+      if ((key & hi_mask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1);
     }
-    __syncthreads();
+    __syncthreads();  // this pass's histogram is complete
+    for (int d = tid; d < 256; d += nt) hn[d] = 0;  // the next pass's, last read in the previous pass
     if (tid < 64) {
       // lane l owns digits 4l..4l+3; suffix sums from the top digit down
-      const int c0 = hist[4 * tid], c1 = hist[4 * tid + 1], c2 = hist[4 * tid + 2], c3 = hist[4 * tid + 3];
+      const int c0 = h[4 * tid], c1 = h[4 * tid + 1], c2 = h[4 * tid + 2], c3 = h[4 * tid + 3];
       const int own = c0 + c1 + c2 + c3;
       int incl = own;  // sum over lanes >= tid
 #pragma unroll
@@ -62,7 +63,7 @@ __device__ inline void radix_kth(const uint32_t* keys, int n, int k, int* hist, 
         if (tid + o < 64) incl += y;
       }
       const int above_lane = incl - own;  // keys in digits above 4*tid+3
-      // the digit d with above(d) < need <= above(d) + hist[d] lies in exactly one lane
+      // the digit d with above(d) < need <= above(d) + h[d] lies in exactly one lane
       int a3 = above_lane, a2 = a3 + c3, a1 = a2 + c2, a0 = a1 + c1;
       int d = -1, ab = 0;
       if (a3 < need && need <= a3 + c3) { d = 4 * tid + 3; ab = a3; }
@@ -70,16 +71,28 @@ __device__ inline void radix_kth(const uint32_t* keys, int n, int k, int* hist, 
       else if (a1 < need && need <= a1 + c1) { d = 4 * tid + 1; ab = a1; }
       else if (a0 < need && need <= a0 + c0) { d = 4 * tid; ab = a0; }
       if (d >= 0) {
-        *sel_digit = d;
-        *sel_above = ab;
+        sel[0] = d;
+        sel[1] = ab;
       }
     }
-    __syncthreads();
-    need -= *sel_above;
-    prefix |= (uint32_t)*sel_digit << shift;
-    __syncthreads();
+    __syncthreads();  // the digit is chosen and the next histogram cleared
+    need -= sel[1];
+    prefix |= (uint32_t)sel[0] << shift;
   }
   T = prefix;
+}
+
+// Merges the softmax partials (m2, s2) into (m1, s1): s is a sum of exp(x - m).
+__device__ inline void merge_softmax(float& m1, float& s1, float m2, float s2) {
+  if (m2 == -INFINITY) return;
+  if (m1 == -INFINITY) {
+    m1 = m2;
+    s1 = s2;
+    return;
+  }
+  const float m = fmaxf(m1, m2);
+  s1 = s1 * __expf(m1 - m) + s2 * __expf(m2 - m);
+  m1 = m;
 }
 
 // FROM_COUNTS: redundancy = counts < beta ? 0 : rowmean (the eviction step);
@@ -98,10 +111,10 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Geom g, const fl
                                                                 const float* __restrict__ sent_pen,
                                                                 const int32_t* __restrict__ sent_id, int s_max) {
   __shared__ uint32_t keys[RKV_MAX_CAPACITY];
-  __shared__ int hist[256];
+  __shared__ int hist[2 * 256];
   __shared__ float fscr[16];
   __shared__ int iscr[16];
-  __shared__ int sel_digit, sel_above;
+  __shared__ int sel[2];
 
   const int slice = blockIdx.x;
   int l, b, h, s0, N;
@@ -119,43 +132,82 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Geom g, const fl
   const size_t base = (size_t)slice * g.n_slots + s0;
   float* fk = (float*)keys;
 
-  // ---- redundancy softmax over the candidates
-  float mx = -INFINITY;
-  for (int i = tid; i < nc; i += nt) {
-    float r;
-    if (FROM_COUNTS)
-      r = counts[base + i] < g.beta ? 0.f : rowmean[base + i];
-    else
-      r = redundancy[base + i];
-    fk[i] = r;
-    mx = fmaxf(mx, r);
-  }
-  mx = block_max(mx, fscr);
-  float sum = 0.f;
-  for (int i = tid; i < nc; i += nt) {
-    const float e = __expf(fk[i] - mx);
-    fk[i] = e;
-    sum += e;
-  }
-  sum = block_sum(sum, fscr);
-  const float inv = 1.f / sum;
-  for (int i = tid; i < nc; i += nt) {
-    const float R = fk[i] * inv;
-    float Z = g.lambda * importance[base + i] - (1.f - g.lambda) * R;
-    if (PEN) {
-      const int sid = sent_id[(size_t)slice * g.capacity + s0 + i];
-      Z -= (sid >= 0 && sid < s_max) ? sent_pen[(size_t)b * s_max + sid] : 0.f;
+  // ---- redundancy softmax over the candidates: one pass keeps each thread's
+  // running max and sum of exp, then the work-group merges them
+  float mx = -INFINITY, sum = 0.f;
+  constexpr int E = 8;  // elements per thread whose loads go out together
+  for (int i0 = tid; i0 < nc; i0 += E * nt) {
+    float rv[E];
+    int cv[E];
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      const int i = min(i0 + u * nt, nc - 1);  // in range; the extra elements are not used
+      if (FROM_COUNTS) {
+        cv[u] = counts[base + i];
+        rv[u] = rowmean[base + i];
+      } else {
+        rv[u] = redundancy[base + i];
+      }
     }
-    keys[i] = order_key(Z);
-    if (z_out) z_out[base + i] = Z;
-    if (r_out) r_out[base + i] = R;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      const int i = i0 + u * nt;
+      if (i < nc) {
+        const float r = FROM_COUNTS ? (cv[u] < g.beta ? 0.f : rv[u]) : rv[u];
+        fk[i] = r;
+        if (r > mx) {
+          sum = (mx == -INFINITY ? 0.f : sum * __expf(mx - r)) + 1.f;
+          mx = r;
+        } else {
+          sum += __expf(r - mx);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) merge_softmax(mx, sum, __shfl_xor(mx, o), __shfl_xor(sum, o));
+  if ((tid & 63) == 0) {
+    fscr[tid >> 6] = mx;
+    fscr[8 + (tid >> 6)] = sum;
+  }
+  __syncthreads();
+  mx = fscr[0];
+  sum = fscr[8];
+  for (int w = 1; w < nt / 64; ++w) merge_softmax(mx, sum, fscr[w], fscr[8 + w]);
+  const float inv = 1.f / sum;
+  for (int i0 = tid; i0 < nc; i0 += E * nt) {
+    float iv[E];
+    int sv[E];
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      const int i = min(i0 + u * nt, nc - 1);
+      iv[u] = importance[base + i];
+      if (PEN) sv[u] = sent_id[(size_t)slice * g.capacity + s0 + i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      const int i = i0 + u * nt;
+      if (i < nc) {
+        const float R = __expf(fk[i] - mx) * inv;
+        float Z = g.lambda * iv[u] - (1.f - g.lambda) * R;
+        if (PEN) {
+          const int sid = sv[u];
+          Z -= (sid >= 0 && sid < s_max) ? sent_pen[(size_t)b * s_max + sid] : 0.f;
+        }
+        keys[i] = order_key(Z);
+        if (z_out) z_out[base + i] = Z;
+        if (r_out) r_out[base + i] = R;
+      }
+    }
   }
   __syncthreads();
 
   // ---- radix select: exact k-th largest key T, and how many keys equal to T to take
   uint32_t T;
   int need;
-  radix_kth(keys, nc, kk, hist, &sel_digit, &sel_above, T, need);
+  radix_kth(keys, nc, kk, hist, sel, T, need);
 
   // ---- keys equal to T: keep the `need` latest ones. Each thread owns a
   // contiguous range of candidates; a suffix count over threads gives every
@@ -223,9 +275,9 @@ __global__ __launch_bounds__(kSelectThreads) void select_sampled_kernel(Geom g, 
                                                                         int keep_newest, int top_k, float inv_temp,
                                                                         int32_t* __restrict__ keep) {
   __shared__ uint32_t keys[RKV_MAX_CAPACITY];
-  __shared__ int hist[256];
+  __shared__ int hist[2 * 256];
   __shared__ int iscr[16];
-  __shared__ int sel_digit, sel_above;
+  __shared__ int sel[2];
 
   const int slice = blockIdx.x;
   int l, b, h, s0, N;
@@ -251,7 +303,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_sampled_kernel(Geom g, 
   {
     uint32_t T;
     int need;
-    radix_kth(keys, nc, K, hist, &sel_digit, &sel_above, T, need);
+    radix_kth(keys, nc, K, hist, sel, T, need);
     int eq_here = 0;
     for (int i = lo; i < hi && i < nc; ++i) eq_here += keys[i] == T;
     int eq_total;
@@ -269,7 +321,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_sampled_kernel(Geom g, 
   // 2. the top kk of the Gumbel keys, then the kept slots in ascending order
   uint32_t T;
   int need;
-  radix_kth(keys, nc, kk, hist, &sel_digit, &sel_above, T, need);
+  radix_kth(keys, nc, kk, hist, sel, T, need);
   int eq_here = 0;
   for (int i = lo; i < hi && i < nc; ++i) eq_here += keys[i] == T;
   int eq_total;
