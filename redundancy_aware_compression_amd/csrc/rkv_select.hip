@@ -225,15 +225,15 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Geom g, const fl
   {
     int ea = eq_after;
     for (int i = hi - 1; i >= lo; --i) {
-      bool sel;
+      bool take;
       if (i >= nc) {
-        sel = true;  // observation window
+        take = true;  // observation window
       } else {
         const uint32_t key = keys[i];
-        sel = key > T || (key == T && ea < need);
+        take = key > T || (key == T && ea < need);
         if (key == T) ++ea;
       }
-      kept_here += sel;
+      kept_here += take;
     }
   }
   int kept_total;
@@ -243,15 +243,15 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Geom g, const fl
     // walk backwards to reuse the suffix count, writing positions from the end of the range
     int pos = out + kept_here;
     for (int i = hi - 1; i >= lo; --i) {
-      bool sel;
+      bool take;
       if (i >= nc) {
-        sel = true;
+        take = true;
       } else {
         const uint32_t key = keys[i];
-        sel = key > T || (key == T && ea < need);
+        take = key > T || (key == T && ea < need);
         if (key == T) ++ea;
       }
-      if (sel && --pos < B) krow[pos] = s0 + i;  // pos < B always; the guard only bounds the write
+      if (take && --pos < B) krow[pos] = s0 + i;  // pos < B always; the guard only bounds the write
     }
   }
 }
@@ -293,7 +293,16 @@ __global__ __launch_bounds__(kSelectThreads) void select_sampled_kernel(Geom g, 
   const int nc = N - keep_newest, kk = B - keep_newest;
   const int K = min(max(top_k, kk), nc);
   const size_t base = (size_t)slice * g.n_slots + s0;
-  for (int i = tid; i < nc; i += nt) keys[i] = order_key(scores[base + i]);
+  constexpr int E = 8;  // loads per thread issued together
+  for (int i0 = tid; i0 < nc; i0 += E * nt) {
+    float sc[E];
+#pragma unroll
+    for (int u = 0; u < E; ++u) sc[u] = scores[base + min(i0 + u * nt, nc - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < E; ++u)
+      if (i0 + u * nt < nc) keys[i0 + u * nt] = order_key(sc[u]);
+  }
   __syncthreads();
   // each thread owns a contiguous range of the valid tokens
   const int seg = (N + nt - 1) / nt;
@@ -309,12 +318,27 @@ __global__ __launch_bounds__(kSelectThreads) void select_sampled_kernel(Geom g, 
     int eq_total;
     const int eq_before = block_exclusive_scan(eq_here, iscr, &eq_total);
     int ea = eq_total - eq_before - eq_here;
-    for (int i = min(hi, nc) - 1; i >= lo; --i) {
-      const uint32_t key = keys[i];
-      const bool sel = key > T || (key == T && ea < need);
-      if (key == T) ++ea;
-      const float u = uniforms[base + i];
-      keys[i] = sel ? order_key(scores[base + i] * inv_temp - logf(-logf(u))) : 0u;
+    // the thread's candidates from the newest down, E at a time (their
+    // uniforms and scores loaded together)
+    for (int c = min(hi, nc) - 1; c >= lo; c -= E) {
+      float uv[E], sv[E];
+#pragma unroll
+      for (int u = 0; u < E; ++u) {
+        const int i = max(c - u, lo);
+        uv[u] = uniforms[base + i];
+        sv[u] = scores[base + i];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < E; ++u) {
+        const int i = c - u;
+        if (i >= lo) {
+          const uint32_t key = keys[i];
+          const bool take = key > T || (key == T && ea < need);
+          if (key == T) ++ea;
+          keys[i] = take ? order_key(sv[u] * inv_temp - logf(-logf(uv[u]))) : 0u;
+        }
+      }
     }
     __syncthreads();
   }
@@ -331,13 +355,13 @@ __global__ __launch_bounds__(kSelectThreads) void select_sampled_kernel(Geom g, 
   {
     int ea = eq_after;
     for (int i = hi - 1; i >= lo; --i) {
-      bool sel = true;  // the newest keep_newest tokens
+      bool take = true;  // the newest keep_newest tokens
       if (i < nc) {
         const uint32_t key = keys[i];
-        sel = key > T || (key == T && ea < need);
+        take = key > T || (key == T && ea < need);
         if (key == T) ++ea;
       }
-      kept_here += sel;
+      kept_here += take;
     }
   }
   int kept_total;
@@ -346,13 +370,13 @@ __global__ __launch_bounds__(kSelectThreads) void select_sampled_kernel(Geom g, 
     int ea = eq_after;
     int pos = out + kept_here;
     for (int i = hi - 1; i >= lo; --i) {
-      bool sel = true;
+      bool take = true;
       if (i < nc) {
         const uint32_t key = keys[i];
-        sel = key > T || (key == T && ea < need);
+        take = key > T || (key == T && ea < need);
         if (key == T) ++ea;
       }
-      if (sel && --pos < B) krow[pos] = s0 + i;
+      if (take && --pos < B) krow[pos] = s0 + i;
     }
   }
 }
