@@ -587,11 +587,15 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
         }
       }
       uint32_t bits[2] = {0u, 0u};  // sign bits of the block's 32 rows per column fragment
-      if (!GATHER && sizeof(T) == 2 && __builtin_expect(!diag, 1)) {
+      if (sizeof(T) == 2 && __builtin_expect(!diag, 1)) {
         // Both 32-row halves' products first, then the first half's epilogue
         // placed between the second half's 16 MFMAs (4 VALU after each): the
-        // epilogue runs in the matrix units' shadow. (With GATHER, or fp32
-        // keys, the extra accumulators would not fit in registers.)
+        // epilogue runs in the matrix units' shadow. (With fp32 keys the extra
+        // accumulators would not fit in registers. With GATHER they take the
+        // last registers and the compiler spills 8 bytes; spill traffic only
+        // adds vector memory operations younger than the rows a wait is for,
+        // and loads return in order, so every computed vmcnt wait stays
+        // sufficient.)
         float nj0[16], nj1[16];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
