@@ -7,9 +7,11 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 with g++ into ``librkv_oracle.so`` next to this file; this module is only its
 ctypes marshalling. Every function is pinned by the ``-m "not gpu"`` tests
 (hand-derived closed forms, textbook special cases, invariants, brute force).
-Parity unpinned by the pages themselves: the exact combination formula and
-the exact protection rule, which the R-KV page does not print; the oracle
-follows the readings stated in its source.
+Parity unpinned by the pages themselves: they print no example, so the
+readings they leave open (the exact combination formula and protection rule,
+which the R-KV page does not print; the sentence penalty's form; the sampled
+draw's parameters; the free-row order of the hole-filling layout) are pinned
+to those readings, stated in the source, not to values the pages give.
 """
 from __future__ import annotations
 

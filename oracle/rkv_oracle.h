@@ -8,7 +8,8 @@
  * Sources (the R-KV pages):
  *   [RKV] R-KV notes page, yoonschallenge.tistory.com/1236 (NeurIPS 2025
  *         poster): opening notes, summary table, Q&A part 2 ("why did time
- *         drop less than expected"), cause 3 (per-128-token compression work).
+ *         drop less than expected"), cause 3 (per-128-token compression work)
+ *         and cause 4 (attention, importance scoring and eviction fused).
  *   [SKV] SkipKV notes page, yoonschallenge.tistory.com/1230: summary table
  *         rows "sentence-level KV storage skipping" and "final eviction score".
  *   [FKV] ForesightKV explainer, gist.science/ko/paper/2602.03203: technical
@@ -17,7 +18,12 @@
  * tie order, padding) the readings below are stated at the point of use.
  *
  * Parity pins: every function is pinned by the CPU tests against hand-derived
- * closed forms, textbook special cases, invariants and brute force.
+ * closed forms, textbook special cases, library routines, invariants and brute
+ * force. Parity unpinned by the pages themselves: they print no example, so
+ * the readings they leave open (the combination formula, the protection rule,
+ * the sentence penalty's form, the sampled draw's parameters, the free-row
+ * order of the hole-filling layout) are pinned to those readings, not to
+ * values the pages give.
  */
 #ifndef RKV_ORACLE_H
 #define RKV_ORACLE_H
