@@ -142,3 +142,41 @@ def test_evict_step_sentences(name):
         else:
             assert all(i in evicted for i in np.nonzero(pen_c > 0.5)[0]), f"{name} {(l, b, h)}: a penalised token stayed"
     print(f"{name}: kept-set differences inside the band: {ndiff}")
+
+
+@pytest.mark.parametrize("dim", [4, 12, 100, 260, 8192])
+def test_sentence_penalty_shapes(dim):
+    """Vector widths that leave partial chunks (4, 12, 100, 260) and the
+    largest accepted (8192); sequences with no sentence, one sentence, two,
+    and more; a repeat planted in each longer sequence. Against the oracle to
+    PEN_TOL, with the threshold exception of test_sentence_penalty_parity."""
+    import redundancy_aware_compression_amd as rkv
+
+    torch, dev = _gpu.torch_dev()
+    rng = np.random.default_rng(dim)
+    counts = np.array([0, 1, 2, 37], np.int32)
+    s_max = 40
+    vec = rng.standard_normal((len(counts), s_max, dim)).astype(np.float32)
+    for b, n in enumerate(counts):
+        if n >= 2:  # the first sentence is repeated by the last, with noise
+            vec[b, n - 1] = vec[b, 0] + np.float32(0.1) * rng.standard_normal(dim).astype(np.float32)
+    w = synth.small("sent_shapes", 140, num_layers=1, batch=len(counts), num_kv_heads=1, group=1, budget=64)
+    pen = torch.full((len(counts) * s_max,), -5.0, dtype=torch.float32, device=dev)
+    rkv.rkv_sentence_penalty(_gpu.params_of(w), _gpu.to_dev(vec), dev_i32(counts), s_max, dim, TAU_S, pen)
+    torch.cuda.synchronize()
+    gpu = pen.cpu().numpy().reshape(len(counts), s_max)
+    for b, n in enumerate(counts):
+        assert np.all(gpu[b, n:] == 0)
+        if n == 0:
+            continue
+        ref = oracle.sentence_penalty(vec[b, :n], TAU_S)
+        v = vec[b, :n].astype(np.float64)
+        cos = (v @ v.T) / np.outer(np.linalg.norm(v, axis=1), np.linalg.norm(v, axis=1))
+        for i in range(n):
+            near = np.any(np.abs(cos[i, i + 1:] - TAU_S) <= PEN_TOL)
+            if gpu[b, i] > 0 and ref[i] > 0:
+                assert abs(gpu[b, i] - ref[i]) <= PEN_TOL, (dim, b, i, gpu[b, i], ref[i])
+            else:
+                assert (gpu[b, i] == 0) == (ref[i] == 0) or near, (dim, b, i, gpu[b, i], ref[i])
+        if n >= 2:
+            assert gpu[b, 0] > 0.9  # the planted repeat
