@@ -31,6 +31,8 @@ SMALL = {
     "small_a4": synth.small("small_a4", 103, num_layers=1, batch=2, num_kv_heads=2, group=3, budget=200, buffer=77,
                             obs_window=4, extra_capacity=40),
     "single_f32": synth.WORKLOADS["single_f32"],
+    # the largest budget the hole-filling compaction takes (its LDS lists: 6 bytes per budget slot)
+    "max_budget": synth.small("hf_max_budget", 141, num_layers=1, batch=1, num_kv_heads=1, group=2, budget=10000),
 }
 
 
