@@ -122,7 +122,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(Geom g, LayerPtrs k, LayerPt
   int l, b, h, s0, N;
   slice_coords(g, slice, l, b, h);
   seq_range(g, seq_start, b, s0, N);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane % LPR, rr = lane / LPR;
+  const int tid = threadIdx.x, lane = tid & 63, c = lane % LPR, rr = lane / LPR;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the row loops branch on scalars
   float* o_out = out + (size_t)slice * G * kHeadDim;
   if (N == 0) {
     for (int e = tid; e < G * kHeadDim; e += NT) o_out[e] = 0.f;
@@ -141,31 +142,39 @@ __global__ __launch_bounds__(NT) void decode_kernel(Geom g, LayerPtrs k, LayerPt
   }
 
   // Rounds of U loads per lane, software-pipelined: the next round is issued
-  // (rows clamped into the slice) before the current one is used, and the
-  // K pass's last prefetch is the V pass's first round, so those loads fly
-  // across the softmax below.
-  auto load_round = [&](uint4(&x)[U], const char* base, int j0) {
+  // before the current one is used, and the K pass's last prefetch is the V
+  // pass's first round, so those loads fly across the softmax below. Each
+  // round is a buffer load through a descriptor rebased to its first row (a
+  // few scalar operations) with the extent of the rows left, so rows past the
+  // slice read as zeros without touching memory, and the per-lane offsets are
+  // loop-invariant: no vector temporaries that could share registers with a
+  // load still in flight.
+  uint32_t voff[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int row = min(j0 + u * RPI + rr, N - 1);
-      x[u] = *(const uint4*)(base + (size_t)row * RB + c * 16);
-    }
+  for (int u = 0; u < U; ++u) voff[u] = (uint32_t)(u * RPI + rr) * RB + (uint32_t)c * 16u;
+  auto load_round = [&](uint4(&x)[U], const char* base, int j0) {
+    const int left = N - j0;  // uniform
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (size_t)j0 * RB, left > 0 ? (uint32_t)left * RB : 0u);
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[u], 0, 0));
   };
   const int jstart = wave * RPI * U;
   uint4 xa[U], xb[U];
   load_round(xa, kb, jstart);
 
-  // ---- logits: lane c < G of each row stores query c's logit and keeps its max
+  // ---- logits: lane c < G of each row stores query c's logit and keeps its max.
+  // The two buffers alternate (no copy from one to the other: a copy would
+  // wait for the prefetch and leave one round in flight).
   float mrun = -INFINITY;
-  for (int j0 = jstart; j0 < N; j0 += STEP) {
+  auto k_round = [&](const uint4(&cur)[U], uint4(&nxt)[U], int j0) {
     const int jn = j0 + STEP;
-    load_round(xb, jn < N ? kb : vb, jn < N ? jn : jstart);
+    load_round(nxt, jn < N ? kb : vb, jn < N ? jn : jstart);
     __builtin_amdgcn_sched_barrier(0);  // the next round's loads go out before this round's work
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float part[G];
 #pragma unroll
-      for (int gi = 0; gi < G; ++gi) part[gi] = row_sum<LPR>(DL::dot(xa[u], qv[gi]));
+      for (int gi = 0; gi < G; ++gi) part[gi] = row_sum<LPR>(DL::dot(cur[u], qv[gi]));
       const int row = j0 + u * RPI + rr;
       if (c < G && row < N) {
         const float lg = DL::PRESCALED ? pick<G>(part, c) : pick<G>(part, c) * qs;
@@ -173,8 +182,15 @@ __global__ __launch_bounds__(NT) void decode_kernel(Geom g, LayerPtrs k, LayerPt
         mrun = fmaxf(mrun, lg);
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) xa[u] = xb[u];
+  };
+  bool v_in_b = false;  // the buffer that holds the V pass's first round
+  for (int j0 = jstart; j0 < N; j0 += 2 * STEP) {
+    k_round(xa, xb, j0);
+    if (j0 + STEP >= N) {
+      v_in_b = true;
+      break;
+    }
+    k_round(xb, xa, j0 + STEP);
   }
 #pragma unroll
   for (int o = LPR; o < 64; o <<= 1) mrun = fmaxf(mrun, __shfl_xor(mrun, o));
@@ -214,23 +230,23 @@ __global__ __launch_bounds__(NT) void decode_kernel(Geom g, LayerPtrs k, LayerPt
     inv[gi] = 1.f / s;
   }
 
-  // ---- output: o[g] = sum_j p_j v_j over the lane's rows and dims (xa holds
-  // the first round of V)
+  // ---- output: o[g] = sum_j p_j v_j over the lane's rows and dims (xa or xb
+  // holds the first round of V)
   float o[G][EPL];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi)
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[gi][e] = 0.f;
-  for (int j0 = jstart; j0 < N; j0 += STEP) {
-    load_round(xb, vb, j0 + STEP);  // past the slice: its last row again, unused
+  auto v_round = [&](const uint4(&cur)[U], uint4(&nxt)[U], int j0) {
+    load_round(nxt, vb, j0 + STEP);  // rows past the slice read as zeros
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int row = j0 + u * RPI + rr;
       const bool ok = row < N;
-      const int rc = ok ? row : N - 1;  // in-bounds index for rows past the slice, weight 0
+      const int rc = ok ? row : N - 1;  // in-bounds LDS index for rows past the slice (zero rows, weight 0)
       float vf[EPL];
-      DL::widen(xa[u], vf);
+      DL::widen(cur[u], vf);
 #pragma unroll
       for (int gi = 0; gi < G; ++gi) {
         const float p = ok ? lw[rc * G + gi] : 0.f;
@@ -238,9 +254,23 @@ __global__ __launch_bounds__(NT) void decode_kernel(Geom g, LayerPtrs k, LayerPt
         for (int e = 0; e < EPL; ++e) o[gi][e] = fmaf(p, vf[e], o[gi][e]);
       }
     }
+  };
+  auto v_pass = [&](uint4(&x0)[U], uint4(&x1)[U]) {
+    for (int j0 = jstart; j0 < N; j0 += 2 * STEP) {
+      v_round(x0, x1, j0);
+      if (j0 + STEP >= N) break;
+      v_round(x1, x0, j0 + STEP);
+    }
+  };
+  // one V loop, starting from xa. Its first round had the whole softmax to
+  // land: wait for it here (vmcnt(0); expcnt, lgkmcnt free), so that no load
+  // is pending into the loop and the loop header needs no wait of its own
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  if (v_in_b) {
 #pragma unroll
     for (int u = 0; u < U; ++u) xa[u] = xb[u];
   }
+  v_pass(xa, xb);
 
   // ---- capture: acc[g][j] += w_gj
   if (acc) {
