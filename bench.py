@@ -362,7 +362,7 @@ def sweep_main(args, w):
 
 
 def sweep_cpu_baseline(ds, w, budget_s: float = 20.0):
-    """The CPU oracle on a sample of round 0's pre-eviction slices (copied
+    """The CPU oracle on a sample of the first eviction's pre-eviction slices (copied
     from the device), one slice per task on a thread pool."""
     from concurrent.futures import ThreadPoolExecutor
 
@@ -399,7 +399,7 @@ def sweep_cpu_baseline(ds, w, budget_s: float = 20.0):
     wall = time.perf_counter() - t
     step_s = wall * w.slices / n
     return {"value": 1.0 / step_s, "unit": "steps/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} of {w.slices} slices of round 0 (score, select, K/V gather), one slice per task on "
+            "sample": f"{n} of {w.slices} slices of the first eviction (score, select, K/V gather), one slice per task on "
                       f"{cores} threads; step time extrapolated from the sample's wall time",
             "ms_per_step": step_s * 1e3, "cpu_seconds": one * n}
 
@@ -794,7 +794,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the eviction step has no cross-GPU exchange and this build runs on a "
+        print("bench.py measures one GPU: the eviction step has no cross-GPU exchange, and the library runs on a "
               "single MI355X; --gpus must be 1", file=sys.stderr)
         sys.exit(2)
 

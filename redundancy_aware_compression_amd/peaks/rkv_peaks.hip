@@ -1,6 +1,6 @@
 // Peak microbenchmarks for the roofline figures of the eviction kernels: the
 // bf16 MFMA issue rate of the chip and its HBM read and copy bandwidth, as
-// this build measures them (the rooflines quote MI355X's published peaks;
+// measured by plain kernels (the rooflines quote MI355X's published peaks;
 // these show how close a plain kernel gets to them).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
