@@ -263,9 +263,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(Geom g, LayerPtrs k, LayerPt
     }
   };
   // one V loop, starting from xa. Its first round had the whole softmax to
-  // land: wait for it here (vmcnt(0); expcnt, lgkmcnt free), so that no load
-  // is pending into the loop and the loop header needs no wait of its own
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  // land: wait for it here, so that no load is pending into the loop and the
+  // loop header needs no wait of its own
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   if (v_in_b) {
 #pragma unroll
     for (int u = 0; u < U; ++u) xa[u] = xb[u];

@@ -85,6 +85,9 @@ __device__ inline void mma_frag(f32x16& acc, const Frag<float>& a, const Frag<fl
   }
 }
 
+// s_waitcnt immediate for vmcnt(v), other counters unconstrained (gfx9 encoding).
+__device__ constexpr int vmcnt_imm(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // Raw buffer descriptors: base address, byte extent and the gfx9 descriptor
 // word 3 for 32-bit raw access (stride 0, no swizzle). Accesses past the
 // extent are range-checked per dword by the hardware: loads return 0 (also

@@ -60,8 +60,6 @@ static_assert(kRowBlock == 8 * kGramWaves, "pre-pass: 8 lanes per row, 8 rows pe
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// s_waitcnt immediate for vmcnt(v), other counters unconstrained (gfx9 encoding).
-__device__ constexpr int vmcnt_imm(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <typename T>
 struct Stage {
