@@ -79,7 +79,7 @@ __device__ inline float row_sum(float v) {
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
-  if constexpr (LPR == 32) v += __shfl_xor(v, 16);
+  if constexpr (LPR == 32) v = xor16_add(v);
   return v;
 }
 
@@ -192,8 +192,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(Geom g, LayerPtrs k, LayerPt
     }
     k_round(xb, xa, j0 + STEP);
   }
-#pragma unroll
-  for (int o = LPR; o < 64; o <<= 1) mrun = fmaxf(mrun, __shfl_xor(mrun, o));
+  if constexpr (LPR == 16) mrun = xor16_max(mrun);  // the rows of the wave (lanes LPR apart)
+  mrun = xor32_max(mrun);
   if (rr == 0 && c < G) red_m[wave][c] = mrun;
   __syncthreads();
   float m[G];
@@ -299,9 +299,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(Geom g, LayerPtrs k, LayerPt
 #pragma unroll
   for (int gi = 0; gi < G; ++gi)
 #pragma unroll
-    for (int e = 0; e < EPL; ++e)
-#pragma unroll
-      for (int s = LPR; s < 64; s <<= 1) o[gi][e] += __shfl_xor(o[gi][e], s);
+    for (int e = 0; e < EPL; ++e) {
+      if constexpr (LPR == 16) o[gi][e] = xor16_add(o[gi][e]);
+      o[gi][e] = xor32_add(o[gi][e]);
+    }
   __syncthreads();  // every wave is done with the weights
   if (rr == 0) {
 #pragma unroll

@@ -175,6 +175,51 @@ __device__ inline const char* row_ptr(const void* layer, const Geom& g, int b, i
   return (const char*)layer + (((size_t)b * g.H + h) * g.capacity + slot) * (size_t)(kHeadDim * Elem<T>::kBytes);
 }
 
+// The value of lane ^ 32 (or lane ^ 16) of a wave, from gfx950's lane-swap
+// instructions: VALU operations, where a general shuffle is an LDS round trip
+// (ds_bpermute). permlane32_swap(a, b) exchanges lanes 32..63 of a with lanes
+// 0..31 of b; with a = b = v its two results hold v's low half twice and its
+// high half twice, and the partner of a lane is the one its own half does not
+// hold. permlane16_swap does the same between the odd and even 16-lane rows.
+// The exec mask must be full (every caller is wave-uniform there).
+__device__ inline uint32_t lane_xor32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
+__device__ inline uint32_t lane_xor16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return (threadIdx.x & 16) ? r[0] : r[1];
+}
+__device__ inline float lane_xor32(float v) { return __uint_as_float(lane_xor32(__float_as_uint(v))); }
+__device__ inline float lane_xor16(float v) { return __uint_as_float(lane_xor16(__float_as_uint(v))); }
+// v + v[lane ^ 32] and max(v, v[lane ^ 32]): the swap's two results are the
+// lane's own value and its partner's, in some order, so no select is needed
+// (addition and max are commutative: the same bits as with the partner).
+__device__ inline float xor32_add(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline uint32_t xor32_add(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return r[0] + r[1];
+}
+__device__ inline float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor16_add(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ inline float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// v + v[lane ^ 8]: within a 16-lane row, rotating by 8 is the xor
+__device__ inline float xor8_add(float v) {
+  return v + __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x128 /* row_ror:8 */, 0xF, 0xF, false));
+}
+
 __device__ inline float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -664,14 +664,14 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       if constexpr (CAPT) break;
-      merge_ms(tM[u], tS[u], __shfl_xor(tM[u], 16), __shfl_xor(tS[u], 16));
-      merge_ms(tM[u], tS[u], __shfl_xor(tM[u], 32), __shfl_xor(tS[u], 32));
+      merge_ms(tM[u], tS[u], lane_xor16(tM[u]), lane_xor16(tS[u]));
+      merge_ms(tM[u], tS[u], lane_xor32(tM[u]), lane_xor32(tS[u]));
     }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      run[e] += __shfl_xor(run[e], 8);
-      run[e] += __shfl_xor(run[e], 16);
-      run[e] += __shfl_xor(run[e], 32);
+      run[e] = xor8_add(run[e]);
+      run[e] = xor16_add(run[e]);
+      run[e] = xor32_add(run[e]);
     }
     float* msc = (float*)s_lds;                  // [wave][tile u][16 rows][2]
     float* usc = msc + kGramWaves * 2 * 16 * 2;  // [wave][128 dims]
@@ -739,7 +739,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
           const int i = cbase + 32 * f + col;
-          const uint32_t c = cnt[f] + __shfl_xor(cnt[f], 32);  // both half-waves hold rows of the column
+          const uint32_t c = xor32_add(cnt[f]);  // both half-waves hold rows of the column
           if (hh == 0 && i < N) {
             const float dot = SRows<T>::dot(accs[f]);
             counts[srow + s0 + i] = (int32_t)c;
@@ -832,7 +832,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
               }
               if (sh == 2 && alpha > 4) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) v[r] += __shfl_xor(v[r], 32);
+                for (int r = 0; r < 16; ++r) v[r] = xor32_add(v[r]);
               }
             }
             if (alpha > 32) {
@@ -853,7 +853,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
                 const uint32_t m = 32u * t + (uint32_t)acc_row(r, hh);
                 sum += ((m * magic) >> 16) == (uint32_t)gq ? v[r] : 0.f;
               }
-              sum += __shfl_xor(sum, 32);
+              sum = xor32_add(sum);
               if (gq == carry_g) sum += carry;
               if ((gq + 1) * alpha > 32 * (t + 1)) {
                 carry = sum;
@@ -866,7 +866,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
         }
         if (pow2) {
           if (alpha > 32) best = tsum;
-          best = fmaxf(best, __shfl_xor(best, 32));
+          best = xor32_max(best);
         }
         if (hh == 0 && i < N) importance[srow + s0 + i] = best / (float)alpha;
       }
