@@ -220,6 +220,26 @@ __device__ inline float xor8_add(float v) {
   return v + __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x128 /* row_ror:8 */, 0xF, 0xF, false));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave in DPP steps (no LDS
+// round trips): within each 16-lane row, shifts by 1, 2, 3, then 4 and 8 on
+// the upper banks; then the last lane of row 0 (2) is broadcast into row 1
+// (3), and lane 31 into rows 2 and 3. Lanes a step does not write add 0.
+// The exec mask must be full.
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ inline int dpp_add_src(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, BANK_MASK, false);
+}
+__device__ inline int wave_prefix_sum(int x) {
+  int s = x + dpp_add_src<0x111, 0xF, 0xF>(x);  // row_shr:1
+  s += dpp_add_src<0x112, 0xF, 0xF>(x);         // row_shr:2
+  s += dpp_add_src<0x113, 0xF, 0xF>(x);         // row_shr:3
+  s += dpp_add_src<0x114, 0xF, 0xE>(s);         // row_shr:4, lanes 4..15 of each row
+  s += dpp_add_src<0x118, 0xF, 0xC>(s);         // row_shr:8, lanes 8..15 of each row
+  s += dpp_add_src<0x142, 0xA, 0xF>(s);         // row_bcast:15 into rows 1 and 3
+  s += dpp_add_src<0x143, 0xC, 0xF>(s);         // row_bcast:31 into rows 2 and 3
+  return s;
+}
+
 __device__ inline float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -263,12 +283,7 @@ __device__ inline float block_sum(float v, float* scratch) {
 // block total. scratch holds 16 ints.
 __device__ inline int block_exclusive_scan(int v, int* scratch, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_prefix_sum(v);  // inclusive, within the wave
   __syncthreads();
   if (lane == 63) scratch[w] = x;
   __syncthreads();

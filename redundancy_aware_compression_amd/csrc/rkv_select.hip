@@ -30,39 +30,43 @@ __device__ inline uint32_t order_key(float z) {
 // Exact k-th largest of keys[0 .. n) (1 <= k <= n) by four 8-bit radix
 // passes over LDS histograms: T is that key and `need` the number of keys
 // equal to T among the top k. Every thread of the work-group takes part and
-// receives both. hist holds two 256-bin histograms: while one pass's digit is
-// found, the other is cleared for the next pass, so each pass needs two
-// barriers. sel[0], sel[1]: the pass's digit and the keys above it. Every
-// read of keys is done when this returns.
+// receives both. hist holds two histograms of 256 bins (kHistInts ints each):
+// while one pass's digit is found, the other is cleared for the next pass, so
+// each pass needs two barriers. Each bin has kHistCopies adjacent counters and
+// a thread adds into copy (tid % kHistCopies): the keys of a slice share their
+// top bits (sign and exponent), so the first passes put nearly every key in a
+// few bins, and same-address LDS atomics serialise. sel[0], sel[1]: the pass's
+// digit and the keys above it. Every read of keys is done when this returns.
+constexpr int kHistCopies = 4;
+constexpr int kHistInts = 256 * kHistCopies;
 __device__ inline void radix_kth(const uint32_t* keys, int n, int k, int* hist, int* sel, uint32_t& T, int& need) {
   const int tid = threadIdx.x, nt = blockDim.x;
   uint32_t prefix = 0;
   need = k;
-  for (int d = tid; d < 256; d += nt) hist[d] = 0;
+  for (int d = tid; d < kHistInts; d += nt) hist[d] = 0;
   __syncthreads();
 #pragma unroll 1
   for (int pass = 0; pass < 4; ++pass) {
-    int* h = hist + (pass & 1) * 256;
-    int* hn = hist + ((pass + 1) & 1) * 256;
+    int* h = hist + (pass & 1) * kHistInts;
+    int* hn = hist + ((pass + 1) & 1) * kHistInts;
     const int shift = 24 - 8 * pass;
     const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
     for (int i = tid; i < n; i += nt) {
       const uint32_t key = keys[i];
-      if ((key & hi_mask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1);
+      if ((key & hi_mask) == prefix) atomicAdd(&h[kHistCopies * ((key >> shift) & 255u) + (tid % kHistCopies)], 1);
     }
     __syncthreads();  // this pass's histogram is complete
-    for (int d = tid; d < 256; d += nt) hn[d] = 0;  // the next pass's, last read in the previous pass
+    for (int d = tid; d < kHistInts; d += nt) hn[d] = 0;  // the next pass's, last read in the previous pass
     if (tid < 64) {
       // lane l owns digits 4l..4l+3; suffix sums from the top digit down
-      const int c0 = h[4 * tid], c1 = h[4 * tid + 1], c2 = h[4 * tid + 2], c3 = h[4 * tid + 3];
+      static_assert(kHistCopies == 4, "one int4 per bin");
+      const int4* h4 = (const int4*)h + 4 * tid;
+      const int4 q0 = h4[0], q1 = h4[1], q2 = h4[2], q3 = h4[3];
+      const int c0 = q0.x + q0.y + q0.z + q0.w, c1 = q1.x + q1.y + q1.z + q1.w, c2 = q2.x + q2.y + q2.z + q2.w,
+                c3 = q3.x + q3.y + q3.z + q3.w;
       const int own = c0 + c1 + c2 + c3;
-      int incl = own;  // sum over lanes >= tid
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_down(incl, o);
-        if (tid + o < 64) incl += y;
-      }
-      const int above_lane = incl - own;  // keys in digits above 4*tid+3
+      const int pre = wave_prefix_sum(own);                       // lanes <= tid
+      const int above_lane = __builtin_amdgcn_readlane(pre, 63) - pre;  // keys in digits above 4*tid+3
       // the digit d with above(d) < need <= above(d) + h[d] lies in exactly one lane
       int a3 = above_lane, a2 = a3 + c3, a1 = a2 + c2, a0 = a1 + c1;
       int d = -1, ab = 0;
@@ -95,6 +99,24 @@ __device__ inline void merge_softmax(float& m1, float& s1, float m2, float s2) {
   m1 = m;
 }
 
+// The merge over the 64 lanes of a wave, every lane receiving it: partners in
+// DPP steps (lanes 1 and 2 apart in a quad, then the mirrored quad of each 8,
+// the mirrored 8 of each row) and the half swaps for rows and halves. The
+// merge is commutative, so both partners of a step hold the same result. The
+// exec mask must be full.
+template <int CTRL>
+__device__ inline float dpp_partner(float v) {
+  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xF, 0xF, false));
+}
+__device__ inline void wave_merge_softmax(float& m, float& s) {
+  merge_softmax(m, s, dpp_partner<0xB1>(m), dpp_partner<0xB1>(s));    // quad_perm [1, 0, 3, 2]
+  merge_softmax(m, s, dpp_partner<0x4E>(m), dpp_partner<0x4E>(s));    // quad_perm [2, 3, 0, 1]
+  merge_softmax(m, s, dpp_partner<0x141>(m), dpp_partner<0x141>(s));  // row_half_mirror
+  merge_softmax(m, s, dpp_partner<0x140>(m), dpp_partner<0x140>(s));  // row_mirror
+  merge_softmax(m, s, lane_xor16(m), lane_xor16(s));
+  merge_softmax(m, s, lane_xor32(m), lane_xor32(s));
+}
+
 // FROM_COUNTS: redundancy = counts < beta ? 0 : rowmean (the eviction step);
 // otherwise read the given redundancy array (the standalone select call).
 // PEN: SkipKV's sentence deduction (SkipKV notes page, summary table row
@@ -111,7 +133,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Geom g, const fl
                                                                 const float* __restrict__ sent_pen,
                                                                 const int32_t* __restrict__ sent_id, int s_max) {
   __shared__ uint32_t keys[RKV_MAX_CAPACITY];
-  __shared__ int hist[2 * 256];
+  __shared__ __align__(16) int hist[2 * kHistInts];
   __shared__ float fscr[16];
   __shared__ int iscr[16];
   __shared__ int sel[2];
@@ -165,8 +187,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Geom g, const fl
       }
     }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) merge_softmax(mx, sum, __shfl_xor(mx, o), __shfl_xor(sum, o));
+  wave_merge_softmax(mx, sum);
   if ((tid & 63) == 0) {
     fscr[tid >> 6] = mx;
     fscr[8 + (tid >> 6)] = sum;
@@ -275,7 +296,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_sampled_kernel(Geom g, 
                                                                         int keep_newest, int top_k, float inv_temp,
                                                                         int32_t* __restrict__ keep) {
   __shared__ uint32_t keys[RKV_MAX_CAPACITY];
-  __shared__ int hist[2 * 256];
+  __shared__ __align__(16) int hist[2 * kHistInts];
   __shared__ int iscr[16];
   __shared__ int sel[2];
 
