@@ -26,6 +26,9 @@ WORKLOADS = {
                                 lengths=("uniform", 200, 384)),
     "small_b96": synth.small("small_b96", 120, num_layers=1, batch=2, num_kv_heads=3, group=4, budget=96, buffer=40),
     "llama8b_b1": synth.WORKLOADS["llama8b_b1"],
+    # the largest capacity: one slice of 16,384 slots (16,376 candidates)
+    "max_capacity": synth.small("max_capacity_sampled", 150, num_layers=1, batch=1, num_kv_heads=1, group=1,
+                                budget=16384 - 128),
 }
 
 
@@ -90,6 +93,67 @@ def test_select_sampled_parity(name, mode):
     if mode == "deterministic":
         assert ndiff == 0
     print(f"{name} {mode}: kept-set differences inside the Gumbel band: {ndiff}")
+
+
+def run_sampled(w, cs, sc, un, L, top_k, T):
+    import redundancy_aware_compression_amd as rkv
+
+    torch, dev = _gpu.torch_dev()
+    keep = torch.full((w.slices * w.budget,), -9, dtype=torch.int32, device=dev)
+    S = torch.from_numpy(cs.seq_start.copy()).to(dev)
+    rkv.rkv_select_sampled(_gpu.params_of(w), _gpu.to_dev(sc.reshape(-1)), _gpu.to_dev(un.reshape(-1)), S,
+                           cs.n_slots, L, top_k, T, keep)
+    torch.cuda.synchronize()
+    return keep.cpu().numpy().reshape(w.slices, w.budget)
+
+
+def check_all_slices(w, cs, sc, un, keep, L, top_k, T, what):
+    ndiff = 0
+    for l in range(w.num_layers):
+        for b in range(w.batch):
+            for h in range(w.num_kv_heads):
+                s = _gpu.slice_index(w, l, b, h)
+                s0, N = int(cs.seq_start[b]), int(cs.lengths[b])
+                x, u = sc[l, b, h, s0:cs.n_slots], un[l, b, h, s0:cs.n_slots]
+                ref = oracle.select_sampled(x, u, w.budget, L, top_k, T)
+                ndiff += check_sampled(_gpu.keep_rel_of(keep[s], s0), ref, x, u, N, w.budget, L, top_k, T,
+                                       f"{what} {(l, b, h)}")
+    return ndiff
+
+
+@pytest.mark.parametrize("mode", ["deterministic", "top_2x"])
+def test_select_sampled_tied_scores(mode):
+    """Scores rounded to multiples of 0.5: most candidates share their score
+    with many others, so the Top-K threshold falls inside a large run of equal
+    keys and the tie rule (the later slot) decides which of them stay. That
+    stage compares the same float32 values on both sides: with top_k equal to
+    budget - L the kept sets must match exactly."""
+    w = WORKLOADS["small_ragged"]
+    cs = synth.build_cache(w, seed=0)
+    sc, un = synth.sampled_inputs(w, seed=2)
+    sc = (np.round(sc * 2.0) / 2.0).astype(np.float32)
+    L = 64
+    kk = w.budget - L
+    top_k = kk if mode == "deterministic" else 2 * kk
+    keep = run_sampled(w, cs, sc, un, L, top_k, 1.0)
+    ndiff = check_all_slices(w, cs, sc, un, keep, L, top_k, 1.0, f"tied {mode}")
+    if mode == "deterministic":
+        assert ndiff == 0
+
+
+@pytest.mark.parametrize("L", [0, 1, 255])
+def test_select_sampled_keep_newest_limits(L):
+    """keep_newest at its limits (0 <= L < budget): no protected window, a
+    window of one, and a single drawn candidate (budget - L = 1)."""
+    w = WORKLOADS["small_ragged"]
+    assert L < w.budget
+    cs = synth.build_cache(w, seed=0)
+    sc, un = synth.sampled_inputs(w, seed=3)
+    for top_k, T in ((0, 1.0), (3 * (w.budget - L), 0.5)):
+        keep = run_sampled(w, cs, sc, un, L, top_k, T)
+        ndiff = check_all_slices(w, cs, sc, un, keep, L, top_k, T, f"L={L} top_k={top_k}")
+        if top_k == 0:  # raised to budget - L: the pure Top-K, exact
+            assert ndiff == 0
 
 
 def test_evict_step_sampled():
