@@ -231,6 +231,62 @@ def test_evict_step(name):
     print(f"{name}: kept-set differences inside the band: {ndiff}")
 
 
+def test_evict_step_degenerate():
+    """One evicting batch with an empty sequence (N = 0), a one-token sequence
+    and zero keys in an evicting sequence, one of them in the observation
+    window. A zero key has no direction (unit key 0): no similarity with any
+    key, row mean 0, logit 0. Scores against the oracle on every slice of the
+    evicting sequence; the short sequences are not scored, keep everything
+    and move right-aligned; compaction bit-exact; keep sets under the band
+    rule."""
+    import redundancy_aware_compression_amd as rkv
+
+    torch, dev = _gpu.torch_dev()
+    w = synth.small("degenerate", 151, num_layers=2, batch=3, num_kv_heads=2, group=4, budget=256)
+    cs = synth.build_cache(w, seed=0)
+    n = cs.n_slots
+    cs.seq_start[0], cs.lengths[0] = n, 0
+    cs.seq_start[1], cs.lengths[1] = n - 1, 1
+    assert cs.lengths[2] == n > w.budget
+    zero_rows = [5, 6, 100, n - 3]
+    cs.K[:, 2, :, zero_rows] = 0
+    dc = _gpu.DevCache.of(cs)
+    imp, red, cnt = _gpu.gpu_score(dc)
+    for l in range(w.num_layers):
+        for h in range(w.num_kv_heads):
+            for b in (0, 1):
+                assert np.all(cnt[_gpu.slice_index(w, l, b, h)] == -7), "short sequences are not scored"
+            s = _gpu.slice_index(w, l, 2, h)
+            ref = _gpu.oracle_slice(cs, l, 2, h)
+            assert np.all(ref.counts[zero_rows] == 0) and np.all(ref.rbar[zero_rows] == 0)
+            _gpu.check_scores(ref, imp[s], red[s], cnt[s], what=f"degenerate {(l, 2, h)}")
+            assert np.all(cnt[s][zero_rows] == 0) and np.all(red[s][zero_rows] == 0)
+    p = _gpu.params_of(w)
+    wsb = rkv.rkv_workspace_bytes(p)
+    koff = rkv.rkv_workspace_keep_offset(p)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    st, ns = rkv.rkv_evict_step(p, dc.k_layers(), dc.v_layers(), dc.Q, dc.seq_start, n, ws, wsb)
+    torch.cuda.synchronize()
+    assert ns == w.budget
+    keep = ws[koff:koff + w.slices * w.budget * 4].view(torch.int32).cpu().numpy().reshape(w.slices, w.budget)
+    s_new = dc.seq_start.cpu().numpy()
+    K1, V1 = _gpu.to_host(dc.K, cs.K.dtype), _gpu.to_host(dc.V, cs.V.dtype)
+    for b in range(w.batch):
+        N = int(cs.lengths[b])
+        kept = min(N, w.budget)
+        assert s_new[b] == w.budget - kept
+        for l in range(w.num_layers):
+            for h in range(w.num_kv_heads):
+                s = _gpu.slice_index(w, l, b, h)
+                row = keep[s]
+                assert np.all(row[: w.budget - kept] == -1)
+                src = row[w.budget - kept:]
+                assert np.array_equal(K1[l, b, h, w.budget - kept:w.budget], cs.K[l, b, h][src])
+                assert np.array_equal(V1[l, b, h, w.budget - kept:w.budget], cs.V[l, b, h][src])
+                _gpu.check_keep(_gpu.keep_rel_of(row, int(cs.seq_start[b])), _gpu.oracle_slice(cs, l, b, h), w, N,
+                                what=f"degenerate {(l, b, h)}")
+
+
 def test_noop_below_trigger():
     """Below budget + buffer nothing is launched and the cache is bit-identical."""
     import redundancy_aware_compression_amd as rkv
