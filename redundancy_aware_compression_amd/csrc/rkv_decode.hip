@@ -204,16 +204,33 @@ __global__ __launch_bounds__(NT) void decode_kernel(Geom g, LayerPtrs k, LayerPt
     for (int w = 1; w < NW; ++w) m[gi] = fmaxf(m[gi], red_m[w][gi]);
   }
 
-  // ---- weights (unnormalised) and their sums
+  // ---- weights (unnormalised) and their sums, by rows: the G weights of a
+  // row are contiguous, and each thread reads RW rows before it computes, so
+  // the LDS round trips overlap
   float ssum[G];
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) ssum[gi] = 0.f;
-  for (int e = tid; e < N * G; e += NT) {
-    const int gi = e % G;
-    const float p = exp2f(lw[e] - pick<G>(m, gi));
-    lw[e] = p;
+  constexpr int RW = 4;
+  for (int j0 = tid; j0 < N; j0 += RW * NT) {
+    float lv[RW][G];
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) ssum[gg] += gi == gg ? p : 0.f;
+    for (int r = 0; r < RW; ++r) {
+      const int j = min(j0 + r * NT, N - 1);  // in range; rows past N are not used
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) lv[r][gi] = lw[j * G + gi];
+    }
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int j = j0 + r * NT;
+      if (j < N) {
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) {
+          const float p = exp2f(lv[r][gi] - m[gi]);
+          lw[j * G + gi] = p;
+          ssum[gi] += p;
+        }
+      }
+    }
   }
 #pragma unroll
   for (int gi = 0; gi < G; ++gi) {

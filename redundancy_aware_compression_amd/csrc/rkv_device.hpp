@@ -245,10 +245,18 @@ __device__ inline float wave_max(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
 }
+// Sum over the 64 lanes, every lane receiving it: DPP within each 16-lane
+// row (lanes 1 and 2 apart in a quad, the mirrored quad of each 8, the
+// mirrored 8 of the row), then the half swaps across rows and halves. Each
+// step adds two partial sums that its two partners hold alike, so every lane
+// ends with the same bits. The exec mask must be full.
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0xB1, 0xF, 0xF, false));   // quad_perm [1, 0, 3, 2]
+  v += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x4E, 0xF, 0xF, false));   // quad_perm [2, 3, 0, 1]
+  v += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x140, 0xF, 0xF, false));  // row_mirror
+  v = xor16_add(v);
+  return xor32_add(v);
 }
 __device__ inline int wave_sum_i(int v) {
 #pragma unroll
