@@ -289,24 +289,27 @@ __global__ __launch_bounds__(NT) void decode_kernel(Geom g, LayerPtrs k, LayerPt
   }
   v_pass(xa, xb);
 
-  // ---- capture: acc[g][j] += w_gj
+  // ---- capture: acc[g][j] += w_gj. Every query's accumulator loads for a
+  // batch of rows go out together (one memory round trip per batch, not per
+  // query); CU rows per thread keep the batch near 16 values.
   if (acc) {
-    constexpr int CU = 4;  // accumulator reads in flight per thread
+    constexpr int CU = 16 / G > 0 ? 16 / G : 1;
+    float* ab = acc + (size_t)slice * G * g.capacity + s0;  // [G][capacity] from the slice's first valid slot
+    for (int j0 = tid; j0 < N; j0 += CU * NT) {
+      float a[G][CU];
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-      float* ab = acc + ((size_t)slice * G + gi) * g.capacity + s0;
-      for (int j0 = tid; j0 < N; j0 += CU * NT) {
-        float a[CU];
+      for (int u = 0; u < CU; ++u) {
+        const int j = min(j0 + u * NT, N - 1);  // in range; rows past N are not used
 #pragma unroll
-        for (int u = 0; u < CU; ++u) {
-          const int j = j0 + u * NT;
-          a[u] = j < N ? ab[j] : 0.f;
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int gi = 0; gi < G; ++gi) a[gi][u] = ab[(size_t)gi * g.capacity + j];
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < CU; ++u) {
-          const int j = j0 + u * NT;
-          if (j < N) ab[j] = fmaf(lw[j * G + gi], inv[gi], a[u]);
+      for (int u = 0; u < CU; ++u) {
+        const int j = j0 + u * NT;
+        if (j < N) {
+#pragma unroll
+          for (int gi = 0; gi < G; ++gi) ab[(size_t)gi * g.capacity + j] = fmaf(lw[j * G + gi], inv[gi], a[gi][u]);
         }
       }
     }
