@@ -221,10 +221,11 @@ __device__ inline float xor8_add(float v) {
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave in DPP steps (no LDS
-// round trips): within each 16-lane row, shifts by 1, 2, 3, then 4 and 8 on
-// the upper banks; then the last lane of row 0 (2) is broadcast into row 1
-// (3), and lane 31 into rows 2 and 3. Lanes a step does not write add 0.
-// The exec mask must be full.
+// round trips): within each 16-lane row, shifts by 1, 2 and 3, then by 4 and
+// 8 on the banks that have a source; then the last lane of each even row is
+// added into the next row (row_bcast:15), and lane 31 into rows 2 and 3
+// (row_bcast:31). Lanes a step does not write add 0. The exec mask must be
+// full.
 template <int CTRL, int ROW_MASK, int BANK_MASK>
 __device__ inline int dpp_add_src(int v) {
   return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, BANK_MASK, false);
@@ -240,11 +241,6 @@ __device__ inline int wave_prefix_sum(int x) {
   return s;
 }
 
-__device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
 // Sum over the 64 lanes, every lane receiving it: DPP within each 16-lane
 // row (lanes 1 and 2 apart in a quad, the mirrored quad of each 8, the
 // mirrored 8 of the row), then the half swaps across rows and halves. Each
@@ -257,34 +253,6 @@ __device__ inline float wave_sum(float v) {
   v += __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), 0x140, 0xF, 0xF, false));  // row_mirror
   v = xor16_add(v);
   return xor32_add(v);
-}
-__device__ inline int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-// Block-wide reductions (blockDim.x a multiple of 64, <= 1024); scratch holds
-// 16 values. Every thread receives the result.
-__device__ inline float block_max(float v, float* scratch) {
-  v = wave_max(v);
-  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) scratch[w] = v;
-  __syncthreads();
-  float r = scratch[0];
-  for (int i = 1; i < nw; ++i) r = fmaxf(r, scratch[i]);
-  return r;
-}
-__device__ inline float block_sum(float v, float* scratch) {
-  v = wave_sum(v);
-  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) scratch[w] = v;
-  __syncthreads();
-  float r = 0.f;
-  for (int i = 0; i < nw; ++i) r += scratch[i];
-  return r;
 }
 
 // Exclusive prefix sum over the block in thread order; *total receives the
