@@ -174,6 +174,39 @@ __global__ __launch_bounds__(kHoleThreads) void holefill_kernel(Geom g, LayerPtr
   block_exscan_hole((nlead << 16) | nstay, red, &both);
   nlead = both >> 16;               // new first valid virtual slot
   nstay = both & 0xFFFF;            // kept tokens already below the budget
+  const int j0 = nlead + nstay;     // first mover
+  const int nmov = B - j0;
+
+  // The movers (the kept tokens past the budget, a suffix of the keep list)
+  // are known now: the first pass of their row loads goes out here, so that
+  // its memory latency hides behind the free-list work below. Piece idx of
+  // the copy is 16 bytes of row m of K (idx < nrow) or V; sources lie at or
+  // past the budget and destinations below it, so no row is both read and
+  // written.
+  const size_t sbase = ((size_t)b * g.H + h) * g.capacity * (size_t)RB;
+  char* kb = (char*)k.p[l] + sbase;
+  char* vb = (char*)v.p[l] + sbase;
+  constexpr int kPass = 16;  // 16-byte copies in flight per thread
+  const int nrow = nmov * U4_ROW, ncopy = 2 * nrow;
+  auto piece = [&](int idx, int& m, int& part, char*& base) {
+    const bool isv = idx >= nrow;
+    const int r = isv ? idx - nrow : idx;
+    m = r / U4_ROW;
+    part = r % U4_ROW;
+    base = isv ? vb : kb;
+  };
+  u32x4n val[kPass];
+#pragma unroll
+  for (int u = 0; u < kPass; ++u) {
+    const int idx = u * kHoleThreads + tid;
+    if (idx < ncopy) {
+      int m, part;
+      char* base;
+      piece(idx, m, part, base);
+      const int src = kl[j0 + m];
+      if (src != 0xFFFF && src >= B) val[u] = load_nt(base + (size_t)src * RB + part * 16);
+    }
+  }
   // 2. physical slots of the kept tokens that stay
   for (int j = tid; j < B; j += kHoleThreads) {
     const int kv = kl[j];
@@ -202,8 +235,6 @@ __global__ __launch_bounds__(kHoleThreads) void holefill_kernel(Geom g, LayerPtr
   // 4. the new order: stayers keep their slot, movers (the kept tokens past
   // the budget, a suffix of the keep list) take the first free slots, the
   // virtual slots before the new start the rest
-  const int j0 = nlead + nstay;  // first mover
-  const int nmov = B - j0;
   for (int j = tid; j < B; j += kHoleThreads) {
     int o;
     if (j < nlead) {
@@ -218,31 +249,36 @@ __global__ __launch_bounds__(kHoleThreads) void holefill_kernel(Geom g, LayerPtr
     }
     orow[j] = o;
   }
-  // 5. move the rows of K and V: sources at or past the budget, destinations
-  // below it, so no row is both read and written
-  const size_t sbase = ((size_t)b * g.H + h) * g.capacity * (size_t)RB;
-  char* kb = (char*)k.p[l] + sbase;
-  char* vb = (char*)v.p[l] + sbase;
-  // (loads of a pass are all issued before its stores: no source is a destination)
-  constexpr int kPass = 16;  // 16-byte copies in flight per thread
-  const int ncopy = 2 * nmov * U4_ROW;
-  for (int i0 = 0; i0 < ncopy; i0 += kPass * kHoleThreads) {
-    u32x4n val[kPass];
-    char* dst[kPass];
+  // 5. move the rows of K and V: the first pass's loads are in flight since
+  // the keep list was read; its stores, then the further passes (loads of a
+  // pass all issued before its stores)
+  auto store_pass = [&](int i0) {
 #pragma unroll
     for (int u = 0; u < kPass; ++u) {
       const int idx = i0 + u * kHoleThreads + tid;
-      const int kvsel = idx / (nmov * U4_ROW), rem = idx % (nmov * U4_ROW);
-      const int m = rem / U4_ROW, part = rem % U4_ROW;
-      const int src = idx < ncopy ? kl[j0 + m] : 0xFFFF;
-      const bool ok = idx < ncopy && m < nfree && src != 0xFFFF && src >= B;
-      char* base = kvsel ? vb : kb;
-      dst[u] = ok ? base + (size_t)fl[m] * RB + part * 16 : nullptr;
-      if (ok) val[u] = load_nt(base + (size_t)src * RB + part * 16);
+      if (idx < ncopy) {
+        int m, part;
+        char* base;
+        piece(idx, m, part, base);
+        const int src = kl[j0 + m];
+        if (m < nfree && src != 0xFFFF && src >= B) store_nt(base + (size_t)fl[m] * RB + part * 16, val[u]);
+      }
     }
+  };
+  store_pass(0);
+  for (int i0 = kPass * kHoleThreads; i0 < ncopy; i0 += kPass * kHoleThreads) {
 #pragma unroll
-    for (int u = 0; u < kPass; ++u)
-      if (dst[u]) store_nt(dst[u], val[u]);
+    for (int u = 0; u < kPass; ++u) {
+      const int idx = i0 + u * kHoleThreads + tid;
+      if (idx < ncopy) {
+        int m, part;
+        char* base;
+        piece(idx, m, part, base);
+        const int src = kl[j0 + m];
+        if (src != 0xFFFF && src >= B) val[u] = load_nt(base + (size_t)src * RB + part * 16);
+      }
+    }
+    store_pass(i0);
   }
   if (l == 0 && h == 0 && tid == 0) seq_start[b] = nlead;
 }
