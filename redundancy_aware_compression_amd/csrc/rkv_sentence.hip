@@ -20,12 +20,13 @@ constexpr int kSentChunk = 4;  // float4 per lane per sentence in one round of l
 // tau_s, else 0 (a zero vector is similar to nothing). fp32 dot products over
 // dim (a multiple of 4, at most kSentMaxDim); sentence i's vector is staged in
 // LDS and the waves take the later sentences in batches.
-__global__ __launch_bounds__(kSentThreads) void sentence_penalty_kernel(const float* __restrict__ vectors,
+template <int NT>
+__global__ __launch_bounds__(NT) void sentence_penalty_kernel(const float* __restrict__ vectors,
                                                                         const int32_t* __restrict__ n_sent,
                                                                         int s_max, int dim, float tau_s,
                                                                         float* __restrict__ penalty) {
   extern __shared__ __align__(16) float hv[];
-  __shared__ float red[kSentThreads / 64];
+  __shared__ float red[NT / 64];
   const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int n = n_sent[b];
   n = n < 0 ? 0 : (n > s_max ? s_max : n);
@@ -36,7 +37,7 @@ __global__ __launch_bounds__(kSentThreads) void sentence_penalty_kernel(const fl
   }
   const float4* vi = (const float4*)(vectors + ((size_t)b * s_max + i) * dim);
   float ss = 0.f;
-  for (int d = tid; d < dim / 4; d += kSentThreads) {
+  for (int d = tid; d < dim / 4; d += NT) {
     const float4 x = vi[d];
     ((float4*)hv)[d] = x;
     ss += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
@@ -46,13 +47,13 @@ __global__ __launch_bounds__(kSentThreads) void sentence_penalty_kernel(const fl
   __syncthreads();
   float ni = 0.f;
 #pragma unroll
-  for (int k = 0; k < kSentThreads / 64; ++k) ni += red[k];
+  for (int k = 0; k < NT / 64; ++k) ni += red[k];
   ni = sqrtf(ni);
   float best = -INFINITY;  // the wave's largest cosine above tau_s
   // Each wave takes kSentBatch later sentences at a time; their loads are
   // independent, so a batch costs about one memory round trip. Indexes past
   // the last sentence re-read sentence n - 1 and are discarded.
-  for (int j0 = i + 1 + w * kSentBatch; j0 < n; j0 += kSentThreads / 64 * kSentBatch) {
+  for (int j0 = i + 1 + w * kSentBatch; j0 < n; j0 += NT / 64 * kSentBatch) {
     float dot[kSentBatch], sj[kSentBatch];
     const float4* vj[kSentBatch];
 #pragma unroll
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(kSentThreads) void sentence_penalty_kernel(const fl
   if (tid == 0) {
     float m = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < kSentThreads / 64; ++k) m = fmaxf(m, red[k]);
+    for (int k = 0; k < NT / 64; ++k) m = fmaxf(m, red[k]);
     *out = m > -INFINITY ? m : 0.f;
   }
 }
@@ -125,8 +126,16 @@ __global__ __launch_bounds__(kSentThreads) void compact_ids_kernel(Geom g, const
 int launch_sentence_penalty(const float* vectors, const int32_t* n_sent, int batch, int s_max, int dim, float tau_s,
                             float* penalty, void* stream) {
   if (batch == 0 || s_max == 0) return 0;
-  hipLaunchKernelGGL(sentence_penalty_kernel, dim3(s_max, batch), dim3(kSentThreads), (size_t)dim * 4,
-                     (hipStream_t)stream, vectors, n_sent, s_max, dim, tau_s, penalty);
+  // A sentence's row of later sentences is split over the waves of its work-
+  // group. With few work-groups (fewer than two per compute unit) wider groups
+  // finish the longest rows in fewer memory round trips; with many, the
+  // narrow ones keep more rows in flight per compute unit.
+  if ((long)s_max * batch < 2L * kCUs)
+    hipLaunchKernelGGL(sentence_penalty_kernel<1024>, dim3(s_max, batch), dim3(1024), (size_t)dim * 4,
+                       (hipStream_t)stream, vectors, n_sent, s_max, dim, tau_s, penalty);
+  else
+    hipLaunchKernelGGL(sentence_penalty_kernel<kSentThreads>, dim3(s_max, batch), dim3(kSentThreads), (size_t)dim * 4,
+                       (hipStream_t)stream, vectors, n_sent, s_max, dim, tau_s, penalty);
   return (int)hipGetLastError();
 }
 
