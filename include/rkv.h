@@ -107,7 +107,12 @@ size_t rkv_workspace_keep_offset(const rkv_params* p);
 /*
  * Importance and redundancy of every valid token of every (layer, sequence,
  * KV head) whose sequence has outgrown the budget (N_b > budget); other
- * sequences' entries are left unchanged.
+ * sequences' entries are left unchanged. Source: R-KV notes page, summary
+ * table row "importance computation" (the attention the observation tokens
+ * pay each cached token, max over the query heads that share a KV head) and
+ * row "redundancy computation" (cosine similarity of a token's key to the
+ * other keys of its head, the most recent similar tokens protected); Q&A part
+ * 2, cause 3 (key normalisation and the all-pairs cosine of each round).
  *   k_layers   HOST array of num_layers device pointers to K caches (read only)
  *   obs_q      observation queries (read only)
  *   seq_start  [batch] int32 first valid slot per sequence (read only)
@@ -119,7 +124,10 @@ size_t rkv_workspace_keep_offset(const rkv_params* p);
  *   redundancy out: rbar_j = 0 if protected, else mean cosine of key j to the
  *              other N_b - 1 valid keys
  *   counts     out, nullable: int32 c_j = #{ newer valid tokens with cosine >
- *              sim_threshold }
+ *              sim_threshold }, the quantity the protection rule tests
+ *              (token j is protected iff c_j < beta). Not one of the method's
+ *              outputs: it is exposed so that callers and tests can see why a
+ *              token is or is not protected; NULL uses the workspace.
  *   ws, ws_bytes  workspace (see rkv_workspace_bytes)
  */
 rkv_status rkv_score(const rkv_params* p, const void* const* k_layers, const void* obs_q, const int32_t* seq_start,
@@ -127,9 +135,13 @@ rkv_status rkv_score(const rkv_params* p, const void* const* k_layers, const voi
                      size_t ws_bytes, void* stream);
 
 /*
- * Selection from given scores. For each (layer, sequence, KV head) with
- * N_b > budget: R = softmax of redundancy over the candidates (the N_b -
- * obs_window oldest valid tokens), Z = lambda*I - (1-lambda)*R, the
+ * Selection from given scores (R-KV notes page, summary table row "final
+ * selection criterion": importance raises a token's score, redundancy lowers
+ * it, lambda = 0.1 works best; opening notes: the observation tokens are
+ * kept and the top-scoring others fill the budget). For each (layer,
+ * sequence, KV head) with N_b > budget: R = softmax of redundancy over the
+ * candidates (the N_b - obs_window oldest valid tokens), Z = lambda*I -
+ * (1-lambda)*R, the
  * budget - obs_window candidates with the largest Z (equal Z: the later slot
  * wins) plus the obs_window newest tokens are kept. With N_b <= budget every
  * valid token is kept. keep[j] receives the source slot of destination slot
@@ -146,7 +158,10 @@ rkv_status rkv_select(const rkv_params* p, const float* importance, const float*
                       void* stream);
 
 /*
- * In-place, order-preserving compaction: for every (layer, sequence, KV
+ * In-place, order-preserving compaction (R-KV notes page, Q&A part 2, cause
+ * 3: the selected entries are copied into the compressed cache; cause 4:
+ * allocation and re-allocation cost, avoided here by moving rows within the
+ * caller's cache): for every (layer, sequence, KV
  * head) row j of K and V in [0, budget) with keep[j] >= 0 receives the bytes
  * of row keep[j]; then seq_start[b] = number of -1 entries of the sequence's
  * keep rows. Rows with keep[j] = -1 and rows >= budget are left as they are.
@@ -158,7 +173,11 @@ rkv_status rkv_compact(const rkv_params* p, void* const* k_layers, void* const* 
                        int32_t* seq_start, int32_t n_slots, void* stream);
 
 /*
- * One decode-time eviction step over all layers, sequences and KV heads.
+ * One decode-time eviction step over all layers, sequences and KV heads
+ * (R-KV notes page, opening notes and summary table row "decoding-time
+ * compression": once budget + buffer tokens are cached, the cache is
+ * compressed back to the budget; Q&A part 2, cause 3: scoring, selection and
+ * copy of one such round).
  * If *n_slots < budget + buffer nothing is launched or written (RKV_OK).
  * Otherwise scoring, selection and compaction run on `stream` and *n_slots
  * becomes budget; afterwards sequence b holds min(N_b, budget) tokens in

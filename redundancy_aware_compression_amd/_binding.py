@@ -130,6 +130,28 @@ def _ptr_array(xs: Sequence) -> ctypes.Array:
     return (ctypes.c_void_p * len(xs))(*[_ptr(x) for x in xs])
 
 
+def _layers(p: RkvParams, xs: Sequence, what: str):
+    """The HOST array of per-layer cache pointers, as a void pointer. The
+    library reads exactly p.num_layers entries, so a shorter list would hand
+    it arbitrary memory as device pointers: the count is checked here, and a
+    tensor entry must hold exactly one layer [batch][num_kv_heads][capacity]
+    [head_dim] of the cache's element type, contiguous."""
+    if 1 <= p.num_layers <= RKV_MAX_LAYERS and len(xs) != p.num_layers:
+        # (an out-of-range num_layers is the library's RKV_ERR_BAD_SHAPE, returned before it reads the array)
+        raise ValueError(f"{what}: {len(xs)} layer pointers for num_layers = {p.num_layers}")
+    elem = 4 if p.dtype == RKV_F32 else 2
+    need = p.batch * p.num_kv_heads * p.capacity * p.head_dim
+    for l, x in enumerate(xs):
+        if x is None:
+            raise ValueError(f"{what}[{l}] is None")
+        if isinstance(x, int) or not hasattr(x, "numel"):
+            continue
+        if x.element_size() != elem or x.numel() != need or not x.is_contiguous():
+            raise ValueError(f"{what}[{l}]: {x.numel()} contiguous elements of {elem} bytes expected "
+                             f"({need}); got {x.numel()} of {x.element_size()} bytes, contiguous={x.is_contiguous()}")
+    return ctypes.cast(_ptr_array(xs), ctypes.c_void_p)
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         import torch
@@ -168,7 +190,7 @@ def rkv_last_hip_error() -> int:
 
 def rkv_score(p: RkvParams, k_layers: Sequence, obs_q, seq_start, n_slots: int, importance, redundancy,
               counts=None, ws=None, ws_bytes: int = 0, stream=None, check: bool = True) -> int:
-    st = _lib().rkv_score(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p), _ptr(obs_q),
+    st = _lib().rkv_score(ctypes.byref(p), _layers(p, k_layers, "k_layers"), _ptr(obs_q),
                           _ptr(seq_start), n_slots, _ptr(importance), _ptr(redundancy), _ptr(counts), _ptr(ws),
                           ws_bytes, _stream(stream))
     return _check(st, "rkv_score") if check else st
@@ -183,8 +205,8 @@ def rkv_select(p: RkvParams, importance, redundancy, seq_start, n_slots: int, ke
 
 def rkv_compact(p: RkvParams, k_layers: Sequence, v_layers: Sequence, keep, seq_start, n_slots: int, stream=None,
                 check: bool = True) -> int:
-    st = _lib().rkv_compact(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
-                            ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(keep), _ptr(seq_start), n_slots,
+    st = _lib().rkv_compact(ctypes.byref(p), _layers(p, k_layers, "k_layers"),
+                            _layers(p, v_layers, "v_layers"), _ptr(keep), _ptr(seq_start), n_slots,
                             _stream(stream))
     return _check(st, "rkv_compact") if check else st
 
@@ -193,8 +215,8 @@ def rkv_evict_step(p: RkvParams, k_layers: Sequence, v_layers: Sequence, obs_q, 
                    ws_bytes: int, stream=None, check: bool = True):
     """Returns (status, n_slots after the step)."""
     ns = ctypes.c_int32(n_slots)
-    st = _lib().rkv_evict_step(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
-                               ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(obs_q), _ptr(seq_start),
+    st = _lib().rkv_evict_step(ctypes.byref(p), _layers(p, k_layers, "k_layers"),
+                               _layers(p, v_layers, "v_layers"), _ptr(obs_q), _ptr(seq_start),
                                ctypes.byref(ns), _ptr(ws), ws_bytes, _stream(stream))
     if check:
         _check(st, "rkv_evict_step")
@@ -208,8 +230,8 @@ def rkv_evict_step_timed(p: RkvParams, k_layers: Sequence, v_layers: Sequence, o
     if len(stage_events) != 4:
         raise ValueError("rkv_evict_step_timed takes 4 events")
     ev = (ctypes.c_void_p * 4)(*stage_events)
-    st = _lib().rkv_evict_step_timed(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
-                                     ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(obs_q),
+    st = _lib().rkv_evict_step_timed(ctypes.byref(p), _layers(p, k_layers, "k_layers"),
+                                     _layers(p, v_layers, "v_layers"), _ptr(obs_q),
                                      _ptr(seq_start), ctypes.byref(ns), _ptr(ws), ws_bytes, _stream(stream),
                                      ctypes.cast(ev, ctypes.c_void_p))
     if check:
@@ -221,8 +243,8 @@ def rkv_evict_step_holefill(p: RkvParams, k_layers: Sequence, v_layers: Sequence
                             n_slots: int, ws, ws_bytes: int, stream=None, check: bool = True):
     """The eviction step in the hole-filling layout; returns (status, n_slots after the step)."""
     ns = ctypes.c_int32(n_slots)
-    st = _lib().rkv_evict_step_holefill(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
-                                        ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(obs_q),
+    st = _lib().rkv_evict_step_holefill(ctypes.byref(p), _layers(p, k_layers, "k_layers"),
+                                        _layers(p, v_layers, "v_layers"), _ptr(obs_q),
                                         _ptr(seq_start), _ptr(order), ctypes.byref(ns), _ptr(ws), ws_bytes,
                                         _stream(stream))
     if check:
@@ -238,8 +260,8 @@ def rkv_evict_step_holefill_timed(p: RkvParams, k_layers: Sequence, v_layers: Se
     if len(stage_events) != 4:
         raise ValueError("rkv_evict_step_holefill_timed takes 4 events")
     ev = (ctypes.c_void_p * 4)(*stage_events)
-    st = _lib().rkv_evict_step_holefill_timed(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
-                                              ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(obs_q),
+    st = _lib().rkv_evict_step_holefill_timed(ctypes.byref(p), _layers(p, k_layers, "k_layers"),
+                                              _layers(p, v_layers, "v_layers"), _ptr(obs_q),
                                               _ptr(seq_start), _ptr(order), ctypes.byref(ns), _ptr(ws), ws_bytes,
                                               _stream(stream), ctypes.cast(ev, ctypes.c_void_p))
     if check:
@@ -249,8 +271,8 @@ def rkv_evict_step_holefill_timed(p: RkvParams, k_layers: Sequence, v_layers: Se
 
 def rkv_compact_holefill(p: RkvParams, k_layers: Sequence, v_layers: Sequence, keep, seq_start, order,
                          n_slots: int, stream=None, check: bool = True) -> int:
-    st = _lib().rkv_compact_holefill(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
-                                     ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(keep),
+    st = _lib().rkv_compact_holefill(ctypes.byref(p), _layers(p, k_layers, "k_layers"),
+                                     _layers(p, v_layers, "v_layers"), _ptr(keep),
                                      _ptr(seq_start), _ptr(order), n_slots, _stream(stream))
     return _check(st, "rkv_compact_holefill") if check else st
 
@@ -267,8 +289,8 @@ def rkv_evict_step_sampled(p: RkvParams, k_layers: Sequence, v_layers: Sequence,
                            stream=None, check: bool = True):
     """The eviction step with the sampled selection; returns (status, n_slots after the step)."""
     ns = ctypes.c_int32(n_slots)
-    st = _lib().rkv_evict_step_sampled(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
-                                       ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(scores),
+    st = _lib().rkv_evict_step_sampled(ctypes.byref(p), _layers(p, k_layers, "k_layers"),
+                                       _layers(p, v_layers, "v_layers"), _ptr(scores),
                                        _ptr(uniforms), _ptr(seq_start), ctypes.byref(ns), keep_newest, top_k,
                                        temperature, _ptr(ws), ws_bytes, _stream(stream))
     if check:
@@ -288,8 +310,8 @@ def rkv_evict_step_sentences(p: RkvParams, k_layers: Sequence, v_layers: Sequenc
                              stream=None, check: bool = True):
     """The eviction step with SkipKV's sentence deduction; returns (status, n_slots after the step)."""
     ns = ctypes.c_int32(n_slots)
-    st = _lib().rkv_evict_step_sentences(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
-                                         ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(obs_q),
+    st = _lib().rkv_evict_step_sentences(ctypes.byref(p), _layers(p, k_layers, "k_layers"),
+                                         _layers(p, v_layers, "v_layers"), _ptr(obs_q),
                                          _ptr(seq_start), ctypes.byref(ns), _ptr(sent_id), _ptr(vectors),
                                          _ptr(n_sent), s_max, dim, tau_s, _ptr(penalty), _ptr(ws), ws_bytes,
                                          _stream(stream))
@@ -301,8 +323,8 @@ def rkv_evict_step_sentences(p: RkvParams, k_layers: Sequence, v_layers: Sequenc
 def rkv_decode_attention(p: RkvParams, k_layers: Sequence, v_layers: Sequence, q, seq_start, n_slots: int, out,
                          imp_acc=None, stream=None, check: bool = True) -> int:
     """Decode attention of the newest token; with imp_acc the weights are added into it."""
-    st = _lib().rkv_decode_attention(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
-                                     ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(q), _ptr(seq_start),
+    st = _lib().rkv_decode_attention(ctypes.byref(p), _layers(p, k_layers, "k_layers"),
+                                     _layers(p, v_layers, "v_layers"), _ptr(q), _ptr(seq_start),
                                      n_slots, _ptr(out), _ptr(imp_acc) if imp_acc is not None else None,
                                      _stream(stream))
     return _check(st, "rkv_decode_attention") if check else st
@@ -313,9 +335,10 @@ def rkv_evict_step_captured(p: RkvParams, k_layers: Sequence, v_layers: Sequence
     """The eviction step with the importance captured by decode attention; returns
     (status, n_slots after the step)."""
     ns = ctypes.c_int32(n_slots)
-    st = _lib().rkv_evict_step_captured(ctypes.byref(p), ctypes.cast(_ptr_array(k_layers), ctypes.c_void_p),
-                                        ctypes.cast(_ptr_array(v_layers), ctypes.c_void_p), _ptr(imp_acc),
+    st = _lib().rkv_evict_step_captured(ctypes.byref(p), _layers(p, k_layers, "k_layers"),
+                                        _layers(p, v_layers, "v_layers"), _ptr(imp_acc),
                                         _ptr(seq_start), ctypes.byref(ns), _ptr(ws), ws_bytes, _stream(stream))
     if check:
         _check(st, "rkv_evict_step_captured")
     return st, ns.value
+

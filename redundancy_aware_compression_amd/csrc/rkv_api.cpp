@@ -56,7 +56,7 @@ rkv::Geom make_geom(const rkv_params* p, int32_t n_slots) {
   g.n_slots = n_slots;
   g.qrows = p->group * p->obs_window;
   g.lambda = p->lambda;
-  g.tau = p->sim_threshold;
+  g.tau = p->sim_threshold == 0.f ? 0.f : p->sim_threshold;  // -0 compares as +0: S > -0 iff S > 0
   return g;
 }
 

@@ -292,12 +292,12 @@ int launch_compact_holefill(const Geom& g, int dtype, const LayerPtrs& k, const 
   hipStream_t s = (hipStream_t)stream;
   const size_t lds = holefill_lds_bytes(g.budget);
   if (dtype == RKV_BF16)
-    hipLaunchKernelGGL(holefill_kernel<bf16_t>, dim3(slices), dim3(kHoleThreads), lds, s, g, k, v, keep, order,
+    RKV_LAUNCH(holefill_kernel<bf16_t>, dim3(slices), dim3(kHoleThreads), lds, s, g, k, v, keep, order,
                        seq_start);
   else
-    hipLaunchKernelGGL(holefill_kernel<float>, dim3(slices), dim3(kHoleThreads), lds, s, g, k, v, keep, order,
+    RKV_LAUNCH(holefill_kernel<float>, dim3(slices), dim3(kHoleThreads), lds, s, g, k, v, keep, order,
                        seq_start);
-  return (int)hipGetLastError();
+  return 0;
 }
 
 int launch_compact(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const int32_t* keep,
@@ -306,12 +306,12 @@ int launch_compact(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs
   if (slices == 0) return 0;
   hipStream_t s = (hipStream_t)stream;
   if (dtype == RKV_BF16)
-    hipLaunchKernelGGL(compact_kernel<bf16_t>, dim3(2 * slices), dim3(kCompactThreads), 0, s, g, k, v, keep,
+    RKV_LAUNCH(compact_kernel<bf16_t>, dim3(2 * slices), dim3(kCompactThreads), 0, s, g, k, v, keep,
                        seq_start);
   else
-    hipLaunchKernelGGL(compact_kernel<float>, dim3(2 * slices), dim3(kCompactThreads), 0, s, g, k, v, keep,
+    RKV_LAUNCH(compact_kernel<float>, dim3(2 * slices), dim3(kCompactThreads), 0, s, g, k, v, keep,
                        seq_start);
-  return (int)hipGetLastError();
+  return 0;
 }
 
 }  // namespace rkv

@@ -352,9 +352,9 @@ static int launch_decode_nt(const Geom& g, const LayerPtrs& k, const LayerPtrs& 
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err) return err;
   }
-  hipLaunchKernelGGL((decode_kernel<T, G, NT>), dim3(g.L * g.batch * g.H), dim3(NT), lds, s, g, k, v, q,
+  RKV_LAUNCH((decode_kernel<T, G, NT>), dim3(g.L * g.batch * g.H), dim3(NT), lds, s, g, k, v, q,
                      seq_start, out, acc);
-  return (int)hipGetLastError();
+  return 0;
 }
 
 template <typename T, int G>

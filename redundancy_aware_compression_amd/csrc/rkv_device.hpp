@@ -5,9 +5,33 @@
 
 #include <hip/hip_runtime.h>
 
+#include <tuple>
+#include <utility>
+
 #include "rkv_internal.hpp"
 
 namespace rkv {
+
+// Launches kernel(args...) and returns the launch's own hipError_t (0 =
+// success). hipLaunchKernel reports the status of this launch; reading
+// hipGetLastError after a triple-chevron launch would also return an error
+// left behind by any earlier, unrelated HIP call of the thread.
+template <typename... P, typename... A>
+inline int launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t stream, A&&... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<P...> t(static_cast<P>(std::forward<A>(a))...);
+  return std::apply(
+      [&](auto&... x) {
+        void* ptrs[] = {(void*)&x...};
+        return (int)hipLaunchKernel((const void*)kernel, grid, block, ptrs, lds, stream);
+      },
+      t);
+}
+#define RKV_LAUNCH(...)                          \
+  do {                                           \
+    const int e_ = launch_kernel(__VA_ARGS__);   \
+    if (e_ != 0) return e_;                      \
+  } while (0)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -52,6 +76,14 @@ __device__ inline float frag_val<bf16_t>(const Frag<bf16_t>& f, int e) {
 template <>
 __device__ inline float frag_val<float>(const Frag<float>& f, int e) {
   return __uint_as_float(((const uint32_t*)&f.v[e >> 2])[e & 3]);
+}
+
+// Negates every value of a fragment (flips the sign bits).
+template <typename T>
+__device__ inline void frag_negate(Frag<T>& f) {
+  const uint32_t m = sizeof(T) == 2 ? 0x80008000u : 0x80000000u;
+#pragma unroll
+  for (int i = 0; i < Frag<T>::kU4; ++i) f.v[i] = make_uint4(f.v[i].x ^ m, f.v[i].y ^ m, f.v[i].z ^ m, f.v[i].w ^ m);
 }
 
 template <typename T>

@@ -37,8 +37,9 @@
 //
 // Epilogue per element of the Gram: one fma, tau*|k_i|*|k_j| - G_ij, whose
 // sign bit is shifted into a per-lane mask, counted once per block. Rows
-// past the slice read as zero keys with norm 0 and give +0, so only the
-// diagonal block needs the j > i mask. The N x N matrix never leaves
+// past the slice read as zero keys with norm 0 and give +0 (for tau < 0 the
+// column keys are held negated and the complement is counted, so that this
+// stays true), so only the diagonal block needs the j > i mask. The N x N matrix never leaves
 // registers; each column belongs to one lane, which stores its count (no
 // atomics).
 //
@@ -50,15 +51,13 @@
 // loads the next group's rows.
 #include <type_traits>
 
-#include "rkv_device.hpp"
+#include "rkv_tiles.hpp"
 
 namespace rkv {
 
 constexpr int kGramThreads = kGramWaves * 64;
 static_assert(RKV_MAX_QROWS <= kRowBlock, "the query rows fill one stage-sized region");
 static_assert(kRowBlock == 8 * kGramWaves, "pre-pass: 8 lanes per row, 8 rows per wave");
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 
 template <typename T>
@@ -91,23 +90,6 @@ __device__ inline void wait_later_blocks(int later) {
   }
 }
 
-// Waits until at most n of this wave's vector memory operations are
-// outstanding (n clamped to [0, 31], which only waits longer).
-__device__ inline void wait_vm(int n) {
-  switch (n < 0 ? 0 : (n < 31 ? n : 31)) {
-#define RKV_VM_CASE(i) \
-  case i:              \
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(i)); break;
-    RKV_VM_CASE(0) RKV_VM_CASE(1) RKV_VM_CASE(2) RKV_VM_CASE(3) RKV_VM_CASE(4) RKV_VM_CASE(5) RKV_VM_CASE(6)
-    RKV_VM_CASE(7) RKV_VM_CASE(8) RKV_VM_CASE(9) RKV_VM_CASE(10) RKV_VM_CASE(11) RKV_VM_CASE(12)
-    RKV_VM_CASE(13) RKV_VM_CASE(14) RKV_VM_CASE(15) RKV_VM_CASE(16) RKV_VM_CASE(17) RKV_VM_CASE(18)
-    RKV_VM_CASE(19) RKV_VM_CASE(20) RKV_VM_CASE(21) RKV_VM_CASE(22) RKV_VM_CASE(23) RKV_VM_CASE(24)
-    RKV_VM_CASE(25) RKV_VM_CASE(26) RKV_VM_CASE(27) RKV_VM_CASE(28) RKV_VM_CASE(29) RKV_VM_CASE(30)
-    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(31)); break;
-#undef RKV_VM_CASE
-  }
-}
-
 // Issues this wave's share of the direct-to-LDS loads of one 64-row block:
 // row r of the block lands at st_rows + r*RB with 16-byte slot p holding the
 // row's bytes [16*(p ^ (r & 15)), +16). voff[q] is the lane's block-invariant
@@ -118,16 +100,6 @@ __device__ inline void issue_rows(uint32_t st_rows, u32x4_t r, const uint32_t* v
   using S = Stage<T>;
 #pragma unroll
   for (int q = 0; q < S::PER; ++q) dma_to_lds16(r, st_rows + (wave * S::PER + q) * 1024, voff[q], soff);
-}
-
-// MFMA operand fragment (32x32 layout) of staged row R, the lane's half hh.
-template <typename T>
-__device__ inline void frag_from_stage(Frag<T>& f, const char* st_rows, int R, int hh) {
-  using S = Stage<T>;
-  const char* row = st_rows + R * S::RB;
-  const int sw = R & 15;
-#pragma unroll
-  for (int s = 0; s < Frag<T>::kU4; ++s) f.v[s] = *(const uint4*)(row + (((hh * (S::SLOTS / 2) + s) ^ sw) * 16));
 }
 
 // 16x16 logit tiles: lane l supplies row (l % 16) of a tile and, per MFMA,
@@ -201,71 +173,6 @@ __device__ inline float sum8_dpp(float v) {
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
   return v;
 }
-
-// Merges the softmax statistics (m2, s2) into (m1, s1).
-__device__ inline void merge_ms(float& m1, float& s1, float m2, float s2) {
-  const float m = fmaxf(m1, m2);
-  if (m == -INFINITY) return;
-  s1 = (m1 > -INFINITY ? s1 * __expf(m1 - m) : 0.f) + (m2 > -INFINITY ? s2 * __expf(m2 - m) : 0.f);
-  m1 = m;
-}
-
-// Similar pairs of one 32x32 tile: d = tau|k_i| |k_j| - G_ij is negative iff
-// S_ij > tau; each sign bit is shifted into a per-lane mask (one alignbit per
-// element, no compare / carry chain), whose bits are counted once per block.
-__device__ inline uint32_t sign_bits(const f32x16& acc, float tn, const float* nj, uint32_t mask) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) mask = __builtin_amdgcn_alignbit(mask, __float_as_uint(fmaf(tn, nj[r], -acc[r])), 31);
-  return mask;
-}
-// The count on the diagonal tile: only pairs whose row (newer token, index
-// jl0 + acc_row within the block) lies after the column (index il).
-__device__ inline uint32_t count_tile_masked(const f32x16& acc, float tn, const float* nj, int jl0, int il, int hh) {
-  uint32_t c = 0;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const uint32_t sb = __float_as_uint(fmaf(tn, nj[r], -acc[r])) >> 31;
-    c += jl0 + acc_row(r, hh) > il ? sb : 0u;
-  }
-  return c;
-}
-
-// The sum of unit keys s as MFMA rows of the key type: for bf16 three rows
-// s_hi + s_mid + s_lo (each the round-to-nearest-even bf16 of what the
-// previous rows leave, so the rows sum to s within 2^-27 |s|), for fp32 s
-// itself. Element d of row r lives at the swizzled slot of a staged row.
-__device__ inline uint32_t f32_to_bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-template <typename T>
-struct SRows;
-template <>
-struct SRows<bf16_t> {
-  static constexpr int RB = kHeadDim * 2;
-  static constexpr int ROWS = 3;
-  __device__ static void write(char* tile, int d, float s) {
-    float rest = s;
-#pragma unroll
-    for (int r = 0; r < 3; ++r) {
-      const uint32_t h = f32_to_bf16_rne(rest);
-      rest -= __uint_as_float(h << 16);
-      const int byte = d * 2;
-      *(uint16_t*)(tile + r * RB + (((byte >> 4) ^ r) << 4) + (byte & 15)) = (uint16_t)h;
-    }
-  }
-  __device__ static float dot(const f32x16& acc) { return (acc[0] + acc[1]) + acc[2]; }
-};
-template <>
-struct SRows<float> {
-  static constexpr int RB = kHeadDim * 4;
-  static constexpr int ROWS = 1;
-  __device__ static void write(char* tile, int d, float s) {
-    const int byte = d * 4;
-    *(float*)(tile + ((byte >> 4) << 4) + (byte & 15)) = s;  // row 0: no swizzle
-  }
-  __device__ static float dot(const f32x16& acc) { return acc[0]; }
-};
 
 // GATHER: the slice's valid tokens are virtual slots [s0, n_slots); virtual
 // slot v < budget is stored at physical slot order[v], v >= budget at v (the
@@ -449,6 +356,15 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   }
 
   const float scale = 1.0f / sqrtf((float)kHeadDim);
+  // tau < 0: the wave holds its column keys negated and counts the newer
+  // tokens with S_ij < tau (tau*|k_i||k_j| - G_ij > 0 becomes a sign test on
+  // |tau||k_i||k_j| + G_ij), then takes the complement over the valid newer
+  // tokens. Rows past the slice (zero keys, norm 0) then give +0 and never
+  // count, whatever the sign of tau. The epilogue's products with the
+  // column keys change sign with them (csgn).
+  const bool negtau = g.tau < 0.f;
+  const float csgn = negtau ? -1.f : 1.f;
+  const float escale = csgn * scale;
   const int alpha = g.alpha;
   const bool pow2 = (alpha & (alpha - 1)) == 0;
   const uint32_t magic = (65536u + (uint32_t)alpha - 1u) / (uint32_t)alpha;  // m / alpha = (m * magic) >> 16 for m < 64
@@ -580,8 +496,9 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
           frag_from_stage(bf[f], st, 32 * f + col, hh);
+          if (negtau) frag_negate(bf[f]);
           nrm_i[f] = ns[32 * f + col];
-          tn[f] = g.tau * fabsf(nrm_i[f]);  // a zero key (norm -1) compares as G = 0
+          tn[f] = fabsf(g.tau) * fabsf(nrm_i[f]);  // a zero key (norm -1) compares as G = 0
         }
       }
       uint32_t bits[2] = {0u, 0u};  // sign bits of the block's 32 rows per column fragment
@@ -741,8 +658,8 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
           const int i = cbase + 32 * f + col;
           const uint32_t c = xor32_add(cnt[f]);  // both half-waves hold rows of the column
           if (hh == 0 && i < N) {
-            const float dot = SRows<T>::dot(accs[f]);
-            counts[srow + s0 + i] = (int32_t)c;
+            const float dot = csgn * SRows<T>::dot(accs[f]);
+            counts[srow + s0 + i] = negtau ? (int32_t)(N - 1 - i) - (int32_t)c : (int32_t)c;
             const float inv = nrm_i[f] > 0.f ? 1.f / nrm_i[f] : 0.f;
             const float self = nrm_i[f] > 0.f ? 1.f : 0.f;
             rowmean[srow + s0 + i] = (dot * inv - self) * inv_nm1;
@@ -805,7 +722,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
             const float4 s23 = *(const float4*)&rst_lds[2 * m0 + 4];
             const float mm[4] = {s01.x, s01.z, s23.x, s23.z}, ss[4] = {s01.y, s01.w, s23.y, s23.w};
 #pragma unroll
-            for (int c = 0; c < 4; ++c) v[4 * a + c] = __expf(acc[4 * a + c] * scale - mm[c]) * ss[c];
+            for (int c = 0; c < 4; ++c) v[4 * a + c] = __expf(acc[4 * a + c] * escale - mm[c]) * ss[c];
             if (!causal_free) {
 #pragma unroll
               for (int c = 0; c < 4; ++c) {
@@ -921,7 +838,7 @@ int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q,
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid(slices), block(kGramThreads);
 #define RKV_GRAM(T, GA, CA)                                                                                   \
-  hipLaunchKernelGGL((gram_kernel<T, GA, CA>), grid, block, 0, s, g, k, obs_q, seq_start, order, imp_acc, \
+  RKV_LAUNCH((gram_kernel<T, GA, CA>), grid, block, 0, s, g, k, obs_q, seq_start, order, imp_acc, \
                      importance, rowmean, counts)
   if (dtype == RKV_BF16) {
     if (order)
@@ -939,7 +856,7 @@ int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q,
       RKV_GRAM(float, false, false);
   }
 #undef RKV_GRAM
-  return (int)hipGetLastError();
+  return 0;
 }
 
 int launch_redundancy(const Geom& g, const int32_t* seq_start, const int32_t* counts, const float* rowmean,
@@ -947,9 +864,9 @@ int launch_redundancy(const Geom& g, const int32_t* seq_start, const int32_t* co
   const int slices = g.L * g.batch * g.H;
   if (slices == 0 || g.n_slots == 0) return 0;
   dim3 grid((g.n_slots + 255) / 256, slices);
-  hipLaunchKernelGGL(redundancy_kernel, grid, dim3(256), 0, (hipStream_t)stream, g, seq_start, counts, rowmean,
+  RKV_LAUNCH(redundancy_kernel, grid, dim3(256), 0, (hipStream_t)stream, g, seq_start, counts, rowmean,
                      redundancy);
-  return (int)hipGetLastError();
+  return 0;
 }
 
 }  // namespace rkv

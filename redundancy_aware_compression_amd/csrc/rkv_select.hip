@@ -406,9 +406,9 @@ int launch_select_sampled(const Geom& g, const float* scores, const float* unifo
                           int keep_newest, int top_k, float temperature, int32_t* keep, void* stream) {
   const int slices = g.L * g.batch * g.H;
   if (slices == 0) return 0;
-  hipLaunchKernelGGL(select_sampled_kernel, dim3(slices), dim3(kSelectThreads), 0, (hipStream_t)stream, g, scores,
+  RKV_LAUNCH(select_sampled_kernel, dim3(slices), dim3(kSelectThreads), 0, (hipStream_t)stream, g, scores,
                      uniforms, seq_start, keep_newest, top_k, 1.f / temperature, keep);
-  return (int)hipGetLastError();
+  return 0;
 }
 
 int launch_select(const Geom& g, const float* importance, const float* redundancy, const int32_t* counts,
@@ -419,15 +419,15 @@ int launch_select(const Geom& g, const float* importance, const float* redundanc
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid(slices), block(kSelectThreads);
   if (counts && sent_pen)
-    hipLaunchKernelGGL((select_kernel<true, true>), grid, block, 0, s, g, importance, redundancy, counts, rowmean,
+    RKV_LAUNCH((select_kernel<true, true>), grid, block, 0, s, g, importance, redundancy, counts, rowmean,
                        seq_start, keep, z_out, r_out, sent_pen, sent_id, s_max);
   else if (counts)
-    hipLaunchKernelGGL((select_kernel<true, false>), grid, block, 0, s, g, importance, redundancy, counts, rowmean,
+    RKV_LAUNCH((select_kernel<true, false>), grid, block, 0, s, g, importance, redundancy, counts, rowmean,
                        seq_start, keep, z_out, r_out, sent_pen, sent_id, s_max);
   else
-    hipLaunchKernelGGL((select_kernel<false, false>), grid, block, 0, s, g, importance, redundancy, counts,
+    RKV_LAUNCH((select_kernel<false, false>), grid, block, 0, s, g, importance, redundancy, counts,
                        rowmean, seq_start, keep, z_out, r_out, sent_pen, sent_id, s_max);
-  return (int)hipGetLastError();
+  return 0;
 }
 
 }  // namespace rkv

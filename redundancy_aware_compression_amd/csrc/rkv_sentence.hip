@@ -131,20 +131,20 @@ int launch_sentence_penalty(const float* vectors, const int32_t* n_sent, int bat
   // finish the longest rows in fewer memory round trips; with many, the
   // narrow ones keep more rows in flight per compute unit.
   if ((long)s_max * batch < 2L * kCUs)
-    hipLaunchKernelGGL(sentence_penalty_kernel<1024>, dim3(s_max, batch), dim3(1024), (size_t)dim * 4,
+    RKV_LAUNCH(sentence_penalty_kernel<1024>, dim3(s_max, batch), dim3(1024), (size_t)dim * 4,
                        (hipStream_t)stream, vectors, n_sent, s_max, dim, tau_s, penalty);
   else
-    hipLaunchKernelGGL(sentence_penalty_kernel<kSentThreads>, dim3(s_max, batch), dim3(kSentThreads), (size_t)dim * 4,
+    RKV_LAUNCH(sentence_penalty_kernel<kSentThreads>, dim3(s_max, batch), dim3(kSentThreads), (size_t)dim * 4,
                        (hipStream_t)stream, vectors, n_sent, s_max, dim, tau_s, penalty);
-  return (int)hipGetLastError();
+  return 0;
 }
 
 int launch_compact_ids(const Geom& g, const int32_t* keep, int32_t* ids, void* stream) {
   const int slices = g.L * g.batch * g.H;
   if (slices == 0) return 0;
-  hipLaunchKernelGGL(compact_ids_kernel, dim3(slices), dim3(kSentThreads), (size_t)g.budget * 4,
+  RKV_LAUNCH(compact_ids_kernel, dim3(slices), dim3(kSentThreads), (size_t)g.budget * 4,
                      (hipStream_t)stream, g, keep, ids);
-  return (int)hipGetLastError();
+  return 0;
 }
 
 }  // namespace rkv

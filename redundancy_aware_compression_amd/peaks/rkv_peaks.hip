@@ -95,23 +95,26 @@ extern "C" {
 
 int rkv_peak_mfma_bf16(int32_t blocks, int32_t iters, float* out, void* stream) {
   if (blocks < 1 || iters < 1 || !out) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(mfma_peak_kernel, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream, iters, out);
-  return (int)hipGetLastError();
+  void* args[] = {&iters, &out};
+  return (int)hipLaunchKernel((const void*)mfma_peak_kernel, dim3(blocks), dim3(kThreads), args, 0, (hipStream_t)stream);
 }
 
 int rkv_peak_hbm_read(const void* src, size_t bytes, int32_t blocks, uint32_t* out, void* stream) {
   if (!src || !out || blocks < 1 || (bytes & 15u) || ((uintptr_t)src & 15u)) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(hbm_read_kernel, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream, (const u32x4*)src,
-                     bytes / 16, out);
-  return (int)hipGetLastError();
+  const u32x4* s4 = (const u32x4*)src;
+  size_t n = bytes / 16;
+  void* args[] = {&s4, &n, &out};
+  return (int)hipLaunchKernel((const void*)hbm_read_kernel, dim3(blocks), dim3(kThreads), args, 0, (hipStream_t)stream);
 }
 
 int rkv_peak_hbm_copy(const void* src, void* dst, size_t bytes, int32_t blocks, void* stream) {
   if (!src || !dst || blocks < 1 || (bytes & 15u) || (((uintptr_t)src | (uintptr_t)dst) & 15u))
     return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(hbm_copy_kernel, dim3(blocks), dim3(kThreads), 0, (hipStream_t)stream, (const u32x4*)src,
-                     (u32x4*)dst, bytes / 16);
-  return (int)hipGetLastError();
+  const u32x4* s4 = (const u32x4*)src;
+  u32x4* d4 = (u32x4*)dst;
+  size_t n = bytes / 16;
+  void* args[] = {&s4, &d4, &n};
+  return (int)hipLaunchKernel((const void*)hbm_copy_kernel, dim3(blocks), dim3(kThreads), args, 0, (hipStream_t)stream);
 }
 
 int rkv_peak_threads_per_block(void) { return kThreads; }

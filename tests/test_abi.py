@@ -311,3 +311,27 @@ def test_peaks_library_exports_its_header():
     assert lib.rkv_peak_hbm_copy(FAKE + 8, FAKE, 4096, 4, None) != 0  # misaligned
     assert lib.rkv_peak_mfma_bf16(0, 10, FAKE, None) != 0  # no work-groups
     assert lib.rkv_peak_threads_per_block() == 256
+
+
+def test_binding_checks_layer_lists():
+    """The binding refuses a per-layer pointer list whose length is not
+    num_layers (the library would read past it) and tensors that are not
+    exactly one contiguous layer of the cache's element type; nothing is
+    called in either case."""
+    import torch
+
+    p = P()
+    with pytest.raises(ValueError):
+        rkv.rkv_compact(p, layers(1), layers(), FAKE, FAKE, 300, stream=0)
+    with pytest.raises(ValueError):
+        rkv.rkv_evict_step(p, layers(), layers(3), FAKE, FAKE, 384, FAKE_WS, 1 << 40, stream=0)
+    one = p.batch * p.num_kv_heads * p.capacity * p.head_dim
+    good = [torch.empty(one, dtype=torch.bfloat16) for _ in range(2)]
+    for bad in ([torch.empty(one - 1, dtype=torch.bfloat16)] * 2, [torch.empty(one, dtype=torch.float32)] * 2,
+                [torch.empty(2 * one, dtype=torch.bfloat16)[::2]] * 2):
+        with pytest.raises(ValueError):
+            rkv.rkv_score(p, bad, FAKE, FAKE, 300, FAKE, FAKE, None, FAKE_WS, 1 << 40, stream=0)
+    # the right tensors pass the binding; the library then rejects the NULL queries
+    assert rkv.rkv_score(p, good, 0, FAKE, 300, FAKE, FAKE, None, FAKE_WS, 1 << 40, stream=0,
+                         check=False) == st_of("RKV_ERR_NULL_ARG")
+
