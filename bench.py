@@ -2,11 +2,13 @@
 """Benchmark of the R-KV decode-time eviction step on one MI355X.
 
 One step = one rkv_evict_step over every (layer, sequence, KV head) slice of
-the workload: scoring (key statistics, Gram, importance and row mean in one
-kernel), selection and in-place compaction, i.e. the whole hot path. Default workload: the Llama-8B-shaped
-GQA cache (32 layers, 8 KV heads, group 4, head_dim 128, batch 1, budget
-1024 + buffer 128, window 8, beta 2, lambda 0.1, tau 0.5), seeded synthetic
-keys with ~30 % repeated spans.
+the workload: scoring (key statistics, Gram, importance and row mean),
+selection and in-place compaction, i.e. the whole hot path. Default
+workload: the largest single-GPU configuration, the Qwen-14B-shaped GQA
+cache (48 layers, 8 KV heads, group 5, head_dim 128, batch 8, budget 4096 +
+buffer 128, window 8, beta 2, lambda 0.1, tau 0.5: the O(B^2) redundancy
+regime), seeded synthetic keys with ~40 % repeated spans; `--workload` picks
+the others (llama8b_b1: the Llama-8B shape at batch 1 and budget 1024).
 
 Timing: W warm-up steps, then K timed steps between two device
 synchronisations. Before every step the pristine pre-eviction cache is
@@ -21,6 +23,10 @@ consecutive kernels and gives each kernel's mean duration, from which the
 roofline fractions are computed; every such mark costs the stream a few
 microseconds, so that pass is not the one the step rate comes from.
 
+After the timed passes: a warm pass (no flush), the compaction alone with
+the flush right before it, and the peak microbenchmarks (measured bf16 MFMA
+and HBM read rates, for fractions beside those of the published peaks).
+
 Prints ONE JSON line. `cpu_baseline` times the CPU oracle on a bounded
 sample of the same workload on the host cores.
 """
@@ -28,6 +34,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+from concurrent.futures import ThreadPoolExecutor
 import hashlib
 import json
 import os
@@ -205,11 +212,14 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def kernel_table(w, ev_lens, moved, means, holefill=False):
+def kernel_table(w, ev_lens, moved, means, holefill=False, peaks=None):
     """Per-kernel algorithmic work per launch, achieved rates against the
     MI355X peaks, and the roofline entry of the dominant kernel. ev_lens: the
     valid lengths of the evicting sequences; moved: rows with keep[j] != j;
-    means: mean milliseconds of the scoring, selection and compaction stages."""
+    means: mean milliseconds of the scoring, selection and compaction stages;
+    peaks: measure_peaks()'s result, for the fractions of the measured peaks
+    beside those of the published ones (the MFMA peak is the bf16 one, so it
+    is not applied to fp32 keys)."""
     e = w.elem_bytes
     D, G, A = w.head_dim, w.group, w.obs_window
     per_seq_slices = w.num_layers * w.num_kv_heads
@@ -230,6 +240,12 @@ def kernel_table(w, ev_lens, moved, means, holefill=False):
     }
     for name, k in kernels.items():
         k["frac"] = k["achieved"] / k["peak"]
+        if peaks is not None:
+            mp = (peaks["peaks"]["mfma_bf16_tflops"] if w.dtype == "bf16" else None) if k["unit"] == "TFLOP/s" \
+                else peaks["peaks"]["hbm_read_gbs"]
+            if mp:
+                k["measured_peak"] = mp
+                k["frac_measured_peak"] = k["achieved"] / mp
         if not (holefill and name == "compact"):  # rocprofv3 FETCH_SIZE + WRITE_SIZE, when summarised
             k["traffic"] = measured_traffic(name, w.name)
     if not holefill:  # the same fraction from counters: MFMA busy cycles over all SIMDs' cycles
@@ -244,6 +260,9 @@ def kernel_table(w, ev_lens, moved, means, holefill=False):
                 "traffic": measured_traffic(dom, w.name) if not (holefill and dom == "compact") else None}
     if dk.get("frac_counters") is not None:
         roofline["frac_counters"] = dk["frac_counters"]
+    if dk.get("frac_measured_peak") is not None:
+        roofline["measured_peak"] = dk["measured_peak"]
+        roofline["frac_measured_peak"] = dk["frac_measured_peak"]
     return kernels, roofline
 
 
@@ -285,11 +304,18 @@ def sweep_main(args, w):
         flush_out = torch.zeros((), dtype=torch.int64, device=dev)
         sp = stream.cuda_stream
         plain, staged, moved = [], [], []
+        lock = None if args.no_cpu_baseline or holefill else SweepOracleLeg(w)
+        gen = ThreadPoolExecutor(1)  # draws round r + 1 while round r runs
+        nxt = gen.submit(sw.begin_round, 0)
         t0 = time.perf_counter()
         for r in range(rounds):
-            ds.next_round(r)
+            rnd = ds.next_round(r, nxt.result())
+            if r + 1 < rounds:
+                nxt = gen.submit(sw.begin_round, r + 1)
             if r == 0 and not args.no_cpu_baseline:
                 cpu = sweep_cpu_baseline(ds, w)
+            if lock is not None:
+                lock.before(ds, rnd)
             torch.sum(flush.view(torch.int64), dim=(0,), out=flush_out)
             ev = hip.create(4)
             if r % 2 == 0:
@@ -313,6 +339,8 @@ def sweep_main(args, w):
                 mv = int((keep >= w.budget).sum().item())  # synchronises the stream
             else:
                 mv = int((keep != ident[None, :]).sum().item())  # synchronises the stream
+            if lock is not None:
+                lock.after(r, keep)
             if r % 2 == 0:
                 plain.append((r, hip.elapsed_ms(ev[0], ev[1])))
             else:
@@ -322,6 +350,9 @@ def sweep_main(args, w):
             if (r + 1) % 25 == 0:
                 print(f"[sweep] round {r + 1}/{rounds}", file=sys.stderr, flush=True)
         wall = time.perf_counter() - t0
+        gen.shutdown()
+        if lock is not None:
+            cpu["oracle_match"] = lock.result()
 
     steady = [ms for r, ms in plain if r >= SWEEP_STEADY_FROM] or [ms for _, ms in plain]
     med = percentile(steady, 50)
@@ -359,6 +390,61 @@ def sweep_main(args, w):
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
+
+
+class SweepOracleLeg:
+    """The sweep's lockstep check, part of the CPU-oracle leg: every round
+    the oracle runs on exact copies of a fixed sample of slices'
+    pre-eviction bytes (synth.sweep_sample: 32 slices, the same every round),
+    and the step's kept sets for them are compared with the oracle's under
+    the acceptance rule (equal sets except candidates inside the tolerance
+    band at the k-th score or on a tau-ambiguous pair). The oracle runs on a
+    thread pool beside the GPU rounds."""
+
+    def __init__(self, w, n: int = 32, threads: int = 16):
+        import synth
+
+        self.w, self.picks = w, synth.sweep_sample(w, n)
+        self.sl = [(l * w.batch + b) * w.num_kv_heads + h for (l, b, h) in self.picks]
+        self.pool = ThreadPoolExecutor(min(threads, os.cpu_count() or 1))
+        self.futs = []
+
+    def before(self, ds, rnd):
+        w, N, G = self.w, self.w.budget + self.w.buffer, self.w.group
+        self.pre = [ds.host(ds.K[l, b, h, :N]) for (l, b, h) in self.picks]
+        self.q = [rnd.Q[l, b, h * G:(h + 1) * G].copy() for (l, b, h) in self.picks]
+
+    def after(self, r, keep_dev):
+        keeps = keep_dev[self.sl].cpu().numpy()
+        for i in range(len(self.picks)):
+            self.futs.append(self.pool.submit(self._one, r, self.pre[i], self.q[i], keeps[i]))
+
+    def _one(self, r, k, q, keep):
+        import numpy as np
+
+        import oracle
+
+        w = self.w
+        N = w.budget + w.buffer
+        ref = oracle.slice_eval(k, q, budget=w.budget, obs_window=w.obs_window, beta=w.beta, lam=w.lam, tau=w.tau,
+                                amb_eps=oracle.TAU_BAND)
+        if np.any(keep < 0):
+            return r, ["a full sequence left a destination slot empty"], 0, []
+        return (r,) + oracle.compare_keep(keep.astype(np.int64), ref, N, w.budget, w.obs_window, w.lam,
+                                          oracle.REL_TOL)
+
+    def result(self):
+        res = [f.result() for f in self.futs]
+        self.pool.shutdown()
+        rounds = sorted({r for r, *_ in res})
+        return {"rounds": len(rounds), "slices_per_round": len(self.picks),
+                "slices": [list(t) for t in self.picks],
+                "slice_rounds_checked": len(res),
+                "band_exceptions": int(sum(n for _, _, n, _ in res)),
+                "outside_band": int(sum(len(o) for _, _, _, o in res)),
+                "structural_problems": int(sum(len(p) for _, p, _, _ in res)),
+                "rule": "kept sets equal to the oracle's (same pre-eviction bytes every round) except candidates "
+                        "within 1e-3 relative of the k-th score or on a pair within 3e-5 of tau"}
 
 
 def sweep_cpu_baseline(ds, w, budget_s: float = 20.0):
@@ -511,12 +597,13 @@ def captured_main(args, w):
     print(json.dumps(out_line), flush=True)
 
 
-def peaks_main(args):
+def measure_peaks(reps: int = 5):
     """Measured peaks of the chip, for context beside the published ones the
     rooflines use: bf16 MFMA flops (four independent 32x32x16 chains per wave,
     2048 work-groups of 4 waves), HBM read (4 GiB, 5x the last-level cache and
-    more) and HBM copy (2 GiB to 2 GiB), each the best of --steps launches
-    between HIP events after one warm-up."""
+    more) and HBM copy (2 GiB to 2 GiB), each the best of `reps` launches
+    between HIP events after one warm-up. Returns the JSON object of
+    `bench.py --peaks`."""
     import torch
 
     from redundancy_aware_compression_amd import build as rkv_build
@@ -534,7 +621,6 @@ def peaks_main(args):
     blocks, iters = 2048, 20000
     hbm_blocks = 4096
     read_bytes, copy_bytes = 4 << 30, 2 << 30
-    reps = max(3, min(args.steps, 10))
 
     def best_ms(fn):
         fn()  # warm-up
@@ -583,7 +669,14 @@ def peaks_main(args):
         "hbm_read": line["peaks"]["hbm_read_gbs"] / HBM_PEAK_GBS,
         "hbm_copy": line["peaks"]["hbm_copy_gbs"] / HBM_PEAK_GBS,
     }
-    print(json.dumps(line), flush=True)
+    del out, buf, red, dst
+    torch.cuda.empty_cache()
+    return line
+
+
+def peaks_main(args):
+    """bench.py --peaks: the measured peaks alone, one JSON line."""
+    print(json.dumps(measure_peaks(max(3, min(args.steps, 10)))), flush=True)
 
 
 def sentences_main(args, w):
@@ -773,10 +866,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama8b_b1")
+    ap.add_argument("--workload", default="qwen14b_b8")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-flush", action="store_true", help="keep inputs warm in the last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured-peak microbenchmarks (fractions against the published peaks only)")
     ap.add_argument("--rounds", type=int, default=0, help="sweep workloads: rounds to run (default: the recipe's)")
     ap.add_argument("--peaks", action="store_true",
                     help="measure the chip's bf16 MFMA issue rate and HBM read / copy bandwidth with the peak "
@@ -832,6 +927,7 @@ def main():
         p = rkv.make_params(w.num_layers, w.batch, w.num_kv_heads, w.group, w.capacity, w.budget, w.buffer,
                             w.obs_window, w.beta, w.lam, w.tau, w.dtype)
         wsb = rkv.rkv_workspace_bytes(p)
+        koff = rkv.rkv_workspace_keep_offset(p)
         ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
         # last-level-cache flush by READING 512 MiB: it leaves clean lines, so
         # the step's own reads are not slowed by write-backs of dirty data (a
@@ -919,17 +1015,40 @@ def main():
                 plain_step(wevs[i])
             torch.cuda.synchronize()
             args.no_flush = False
+        # the compaction alone, the last-level cache flushed right before it:
+        # the keep lists the last step left in the workspace (the same every
+        # step) on the restored cache, so none of its reads can hit lines the
+        # scoring kernel brought in
+        cevs = []
+        if not holefill:
+            keep_ws = ws[koff:koff + w.slices * w.budget * 4]
+            cevs = [hip.create(2) for _ in range(args.steps)]
+            for i in range(args.steps):
+                prepare()
+                hip.record(cevs[i][0], sp)
+                rkv.rkv_compact(p, k_layers, v_layers, keep_ws, S, n, stream=stream)
+                hip.record(cevs[i][1], sp)
+            torch.cuda.synchronize()
 
     step_ms = [hip.elapsed_ms(e[0], e[1]) for e in evs]
     staged_ms = [hip.elapsed_ms(e[0], e[3]) for e in sevs]
     stage_ms = [[hip.elapsed_ms(e[s], e[s + 1]) for e in sevs] for s in range(3)]
     warm_ms = [hip.elapsed_ms(e[0], e[1]) for e in wevs]
-    for e in evs + sevs + wevs + [warm]:
+    compact_ms = [hip.elapsed_ms(e[0], e[1]) for e in cevs]
+    for e in evs + sevs + wevs + cevs + [warm]:
         hip.destroy(e)
     mean_ms = sum(step_ms) / len(step_ms)
+    peaks = None if args.no_peaks else measure_peaks()
 
     kernels, roofline = kernel_table(w, [int(cs.lengths[b]) for b in range(w.batch) if cs.lengths[b] > w.budget],
-                                     moved, [sum(x) / len(x) for x in stage_ms], holefill=holefill)
+                                     moved, [sum(x) / len(x) for x in stage_ms], holefill=holefill, peaks=peaks)
+    if compact_ms:
+        c_ms = sum(compact_ms) / len(compact_ms)
+        kb = kernels["compact"]["bytes"]
+        kernels["compact"]["standalone_flushed"] = {
+            "us": c_ms * 1e3, "achieved": kb / (c_ms * 1e-3) / 1e9, "unit": "GB/s",
+            "frac": kb / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "note": "rkv_compact alone, the 512 MiB read flushing the last-level cache right before it"}
 
     out = {
         "metric": METRIC,
@@ -959,6 +1078,8 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
     }
+    if peaks is not None:
+        out["measured_peaks"] = peaks["peaks"]
     if warm_ms:
         out["warm"] = {"us_per_step": sum(warm_ms) / len(warm_ms) * 1e3, "us_median": percentile(warm_ms, 50) * 1e3,
                        "us_p10": percentile(warm_ms, 10) * 1e3, "us_p90": percentile(warm_ms, 90) * 1e3,

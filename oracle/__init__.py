@@ -261,3 +261,56 @@ def decode_attention(keys: np.ndarray, values: np.ndarray, queries: np.ndarray):
     if rc != 0:
         raise ValueError("orc_decode_attention rejected its arguments")
     return out, w
+
+
+# The acceptance rule of a GPU result against the oracle on the same bytes.
+# |S_ij - tau| below TAU_BAND can flip the similarity decision between fp32
+# accumulation and double: 128 exact products summed in fp32 carry a relative
+# error of at most ~128 * 2^-24 of sum |k_i[d] k_j[d]| <= |k_i||k_j|, plus
+# ~1e-7 from each norm, i.e. below 1.6e-5 in S; 3e-5 leaves headroom. Scores
+# are compared to REL_TOL relative.
+TAU_BAND = 3e-5
+REL_TOL = 1e-3
+
+
+def band_exceptions(ref: SliceResult, N: int, budget: int, obs_window: int, lam: float, rel_tol: float) -> np.ndarray:
+    """The acceptance rule's exceptions among a slice's candidates: those whose
+    oracle Z lies within eps_i + eps_k of the k-th largest Z (eps_i =
+    rel_tol (lam |I_i| + (1 - lam) |R_i|), k = budget - obs_window, ties by
+    the later slot), and those on a tau-ambiguous pair. Boolean [N - obs_window]."""
+    nc, k = N - obs_window, budget - obs_window
+    Z, I, R = ref.Z[:nc], ref.importance[:nc], ref.R[:nc]
+    eps = rel_tol * (lam * np.abs(I) + (1 - lam) * np.abs(R))
+    order = sorted(range(nc), key=lambda i: (-Z[i], -i))
+    kth = order[k - 1]
+    ex = np.abs(Z - Z[kth]) <= eps + eps[kth]
+    return ex | ref.ambiguous[:nc].astype(bool)
+
+
+def compare_keep(keep_rel: np.ndarray, ref: SliceResult, N: int, budget: int, obs_window: int, lam: float,
+                 rel_tol: float):
+    """A kept set (positions within the slice, ascending) against the oracle's
+    under the acceptance rule. Returns (problems, n_diff, outside): problems
+    lists structural violations (size, order, window), n_diff the candidates
+    in one set only, outside those of them not excepted by band_exceptions."""
+    problems = []
+    keep_rel = np.asarray(keep_rel)
+    if len(keep_rel) != min(N, budget):
+        problems.append(f"kept {len(keep_rel)} != {min(N, budget)}")
+        return problems, 0, []
+    if np.any(np.diff(keep_rel) <= 0):
+        problems.append("keep not strictly ascending")
+    if N <= budget:
+        if not np.array_equal(keep_rel, np.arange(N)):
+            problems.append("a short sequence must keep every token")
+        return problems, 0, []
+    if not set(range(N - obs_window, N)) <= set(keep_rel.tolist()):
+        problems.append("observation window not kept")
+    g = set(int(x) for x in keep_rel if x < N - obs_window)
+    r = set(int(x) for x in ref.keep if x < N - obs_window)
+    diff = g ^ r
+    outside = []
+    if diff:
+        ex = band_exceptions(ref, N, budget, obs_window, lam, rel_tol)
+        outside = sorted(i for i in diff if not ex[i])
+    return problems, len(diff), outside

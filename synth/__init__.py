@@ -460,6 +460,24 @@ class Sweep:
         self._map(one)
 
 
+def sweep_sample(w: Workload, n: int = 32, seed: int = 11) -> list:
+    """The fixed set of (layer, sequence, KV head) slices a sweep is checked
+    on in every round: the first, a middle (L / 2 - 1) and the last layer x
+    every KV head of sequence 0, then seeded random slices up to n."""
+    L, H = w.num_layers, w.num_kv_heads
+    picks = []
+    for l in (0, L // 2 - 1, L - 1):
+        for h in range(H):
+            if (l, 0, h) not in picks:
+                picks.append((l, 0, h))
+    rng = np.random.default_rng(seed)
+    while len(picks) < min(n, w.slices):
+        t = (int(rng.integers(L)), int(rng.integers(w.batch)), int(rng.integers(H)))
+        if t not in picks:
+            picks.append(t)
+    return picks[:n]
+
+
 class DeviceSweep:
     """The sweep's cache resident on a torch device: K and V
     [L][b][H][capacity][D] and the observation queries, as the eviction step
@@ -504,10 +522,15 @@ class DeviceSweep:
     def v_layers(self):
         return [self.V[l] for l in range(self.w.num_layers)]
 
-    def next_round(self, r: int) -> SweepRound:
+    def next_round(self, r: int, rnd: Optional[SweepRound] = None) -> SweepRound:
+        """Appends round r; rnd, when given, is self.sweep.begin_round(r)
+        drawn ahead of time (it reads nothing the eviction changes, so a
+        caller may draw round r + 1 while round r is evicted and checked)."""
         torch, w = self.torch, self.w
         assert self.n_slots == w.budget, "the previous round was not evicted"
-        rnd = self.sweep.begin_round(r)
+        if rnd is None:
+            rnd = self.sweep.begin_round(r)
+        assert rnd.r == r
         rows = torch.from_numpy(rnd.window_rows(w)).to(self.dev)
         if self.order is not None:  # virtual retained slots -> physical rows
             sl, v = rows // w.capacity, rows % w.capacity

@@ -21,10 +21,11 @@ import synth
 pytestmark = pytest.mark.gpu
 
 
-def run_sweep(w, rounds, pick, threads=8):
+def run_sweep(w, rounds, picks, threads=8):
     """Runs `rounds` eviction rounds of workload w on the device, checking
-    the slices pick(r) returns ([(l, b, h)]) every round. Returns the total
-    number of kept-set differences inside the band."""
+    the slices `picks` ([(l, b, h)]) every round. The host draws round r + 1
+    while round r is evicted and checked. Returns (slices checked, kept-set
+    differences inside the band)."""
     import redundancy_aware_compression_amd as rkv
 
     torch, dev = _gpu.torch_dev()
@@ -36,11 +37,14 @@ def run_sweep(w, rounds, pick, threads=8):
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     keep_all = ws[koff:koff + w.slices * w.budget * 4].view(torch.int32).view(w.slices, w.budget)
     B, N, G = w.budget, w.budget + w.buffer, w.group
-    ndiff = 0
-    with ThreadPoolExecutor(threads) as pool:
+    sl = [_gpu.slice_index(w, *t) for t in picks]
+    ndiff = nchecked = 0
+    with ThreadPoolExecutor(threads) as pool, ThreadPoolExecutor(1) as gen:
+        nxt = gen.submit(sw.begin_round, 0)
         for r in range(rounds):
-            rnd = ds.next_round(r)
-            picks = pick(r)
+            rnd = ds.next_round(r, nxt.result())
+            if r + 1 < rounds:
+                nxt = gen.submit(sw.begin_round, r + 1)
             pre = [(ds.host(ds.K[l, b, h, :N]), ds.host(ds.V[l, b, h, :N])) for (l, b, h) in picks]
             st, ns = rkv.rkv_evict_step(p, ds.k_layers(), ds.v_layers(), ds.Q, ds.seq_start, ds.n_slots, ws, wsb)
             assert ns == B, f"round {r}: n_slots {ns}"
@@ -51,15 +55,16 @@ def run_sweep(w, rounds, pick, threads=8):
                 pre[i][0], rnd.Q[picks[i][0], picks[i][1], picks[i][2] * G:(picks[i][2] + 1) * G], budget=B,
                 obs_window=w.obs_window, beta=w.beta, lam=w.lam, tau=w.tau, amb_eps=_gpu.TAU_BAND),
                 range(len(picks)))
-            for (l, b, h), (k0, v0), ref in zip(picks, pre, refs):
+            keeps = keep_all[sl].cpu().numpy()
+            post = [(ds.host(ds.K[l, b, h, :B]), ds.host(ds.V[l, b, h, :B])) for (l, b, h) in picks]
+            for (l, b, h), (k0, v0), ref, keep, (k1, v1) in zip(picks, pre, refs, keeps, post):
                 what = f"round {r} slice {(l, b, h)}"
-                s = _gpu.slice_index(w, l, b, h)
-                keep = keep_all[s].cpu().numpy()
                 assert np.all(keep >= 0), f"{what}: full sequences keep every destination slot"
                 ndiff += _gpu.check_keep(keep.astype(np.int64), ref, w, N, what=what)
-                assert np.array_equal(ds.host(ds.K[l, b, h, :B]), k0[keep]), f"{what}: K rows"
-                assert np.array_equal(ds.host(ds.V[l, b, h, :B]), v0[keep]), f"{what}: V rows"
-    return ndiff
+                assert np.array_equal(k1, k0[keep]), f"{what}: K rows"
+                assert np.array_equal(v1, v0[keep]), f"{what}: V rows"
+                nchecked += 1
+    return nchecked, ndiff
 
 
 REDUCED = {
@@ -76,21 +81,20 @@ REDUCED = {
 def test_sweep_every_round_every_slice(name):
     w = REDUCED[name]
     every = [(l, b, h) for l in range(w.num_layers) for b in range(w.batch) for h in range(w.num_kv_heads)]
-    ndiff = run_sweep(w, synth.SweepRecipe().rounds, lambda r: every)
-    print(f"{name}: kept-set differences inside the band over 125 rounds: {ndiff}")
+    n, ndiff = run_sweep(w, synth.SweepRecipe().rounds, every)
+    print(f"{name}: {n} slice-rounds checked; kept-set differences inside the band: {ndiff}")
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["llama8b_b16_sweep10pct", "llama8b_b16_sweep1024"])
 def test_sweep_full_shape(name):
-    """The full 32-layer, batch-16 shape over its first rounds, sampled
-    slices (a different set each round, always including the corners)."""
+    """The full 32-layer, batch-16 shape over all 125 rounds, the same 32
+    slices checked in lockstep every round: layers 0, 15 and 31 x every KV
+    head of sequence 0, plus seeded random slices."""
     w = synth.WORKLOADS[name]
-    rng = np.random.default_rng(5)
-
-    def pick(r):
-        extra = [(int(rng.integers(w.num_layers)), int(rng.integers(w.batch)), int(rng.integers(w.num_kv_heads)))
-                 for _ in range(2)]
-        return [(0, 0, 0), (w.num_layers - 1, w.batch - 1, w.num_kv_heads - 1)] + extra
-
-    ndiff = run_sweep(w, 4, pick, threads=16)
-    print(f"{name}: kept-set differences inside the band: {ndiff}")
+    picks = synth.sweep_sample(w, 32)
+    assert len(picks) == 32
+    n, ndiff = run_sweep(w, synth.SweepRecipe().rounds, picks, threads=16)
+    assert n == 32 * synth.SweepRecipe().rounds
+    print(f"{name}: {n} slice-rounds checked (32 slices x 125 rounds); kept-set differences inside the band: "
+          f"{ndiff}, outside: 0")
