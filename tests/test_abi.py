@@ -335,3 +335,25 @@ def test_binding_checks_layer_lists():
     assert rkv.rkv_score(p, good, 0, FAKE, 300, FAKE, FAKE, None, FAKE_WS, 1 << 40, stream=0,
                          check=False) == st_of("RKV_ERR_NULL_ARG")
 
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Loading librkv before torch is imported must not map a second HIP
+    runtime beside the one torch brings (librkv's launches would then go
+    through a runtime that cannot use the device torch has opened)."""
+    import subprocess
+    import sys
+    import textwrap
+
+    code = textwrap.dedent('''
+        import redundancy_aware_compression_amd as rkv
+        rkv.rkv_workspace_bytes(rkv.make_params(2, 2, 2, 4, 384, 256))  # loads librkv
+        import torch
+        from redundancy_aware_compression_amd._binding import hip_runtimes_mapped
+        m = hip_runtimes_mapped()
+        assert len(m) == 1, m
+        print("one runtime:", m.pop())
+    ''')
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stderr[-2000:]
