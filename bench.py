@@ -608,7 +608,9 @@ def measure_peaks(reps: int = 5):
 
     from redundancy_aware_compression_amd import build as rkv_build
 
-    lib = ctypes.CDLL(rkv_build.PEAKS_LIB_PATH)
+    from redundancy_aware_compression_amd._binding import load_hip_library
+
+    lib = load_hip_library(rkv_build.PEAKS_LIB_PATH)
     lib.rkv_peak_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     lib.rkv_peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_void_p]

@@ -74,25 +74,32 @@ def hip_runtimes_mapped() -> set:
         return {line.split()[-1] for line in f if "libamdhip64" in line.split()[-1]}
 
 
+def load_hip_library(path: str) -> ctypes.CDLL:
+    """Loads a HIP library built here (librkv, the peak microbenchmarks).
+    They need the HIP runtime by soname. torch ships its own copy; if such a
+    library were loaded first, the system copy would be mapped and torch
+    would map its own beside it: two runtimes in one process, the library's
+    launches going through one that cannot use the device torch has opened.
+    Mapping torch's first makes the library bind to it; loading refuses when
+    more than one runtime is mapped all the same."""
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    L = ctypes.CDLL(path)
+    runtimes = hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError(f"more than one HIP runtime is mapped into this process: {sorted(runtimes)}; load "
+                          "this package's libraries after torch, or without torch in the process")
+    return L
+
+
 def _lib():
     global _handle
     if _handle is None:
         if not os.path.exists(_LIB):
             raise ImportError(f"librkv.so is not built at {_LIB}; run `python -m redundancy_aware_compression_amd.build`")
-        # librkv needs the HIP runtime by soname. torch ships its own copy; if
-        # librkv were loaded first, the system copy would be mapped and torch
-        # would map its own beside it: two runtimes in one process, and
-        # librkv's launches would go through one that cannot use the device
-        # torch has opened. Mapping torch's first makes librkv bind to it.
-        try:
-            import torch  # noqa: F401
-        except ImportError:
-            pass
-        L = ctypes.CDLL(_LIB)
-        runtimes = hip_runtimes_mapped()
-        if len(runtimes) > 1:
-            raise ImportError(f"more than one HIP runtime is mapped into this process: {sorted(runtimes)}; "
-                              "load librkv (import this package) after torch, or without torch in the process")
+        L = load_hip_library(_LIB)
         P = ctypes.POINTER(RkvParams)
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         L.rkv_workspace_bytes.restype = sz

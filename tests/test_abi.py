@@ -8,6 +8,7 @@ import re
 import pytest
 
 import redundancy_aware_compression_amd as rkv
+from redundancy_aware_compression_amd._binding import load_hip_library
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rkv.h")
@@ -32,7 +33,7 @@ def test_header_declares_the_entry_points():
 
 
 def test_library_exports_every_declared_symbol():
-    lib = ctypes.CDLL(rkv.library_path())
+    lib = load_hip_library(rkv.library_path())
     for name in declared_functions():
         assert hasattr(lib, name), f"librkv.so does not export {name}"
 
@@ -299,7 +300,7 @@ def test_peaks_library_exports_its_header():
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "rkv_peaks.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(rkv_peak_[a-z_0-9]+)\s*\(", text)))
     assert {"rkv_peak_mfma_bf16", "rkv_peak_hbm_read", "rkv_peak_hbm_copy"} <= set(names)
-    lib = ctypes.CDLL(rkv_build.PEAKS_LIB_PATH)
+    lib = load_hip_library(rkv_build.PEAKS_LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
     lib.rkv_peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
