@@ -24,7 +24,9 @@
  * CONVENTIONS (every entry point)
  *   Memory. Every pointer is a DEVICE pointer unless marked HOST. The caller
  *   owns all memory; the library never allocates or frees device memory and
- *   keeps no state between calls except a thread-local last HIP error.
+ *   keeps no state between calls except a thread-local last HIP error and
+ *   the built-in workspace of rkv_evict_step_noalloc (a device array in the
+ *   code object, not an allocation).
  *   Layout. Per-layer caches K and V are [batch][num_kv_heads][capacity]
  *   [head_dim] rows, contiguous (row stride head_dim elements), 16-byte
  *   aligned. Sequence b holds N_b = n_slots - seq_start[b] valid tokens in
@@ -365,6 +367,28 @@ rkv_status rkv_decode_attention(const rkv_params* p, const void* const* k_layers
 rkv_status rkv_evict_step_captured(const rkv_params* p, void* const* k_layers, void* const* v_layers,
                                    const float* imp_acc, int32_t* seq_start, int32_t* n_slots, void* ws,
                                    size_t ws_bytes, void* stream);
+
+/*
+ * rkv_evict_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Exactly rkv_evict_step (same trigger, kernels, results, n_slots and
+ * seq_start updates) with no ws argument: the workspace is a device array of
+ * RKV_NOALLOC_WORKSPACE_BYTES built into the library, which every GPU the
+ * library runs on holds until the process ends. The call allocates nothing
+ * (no hipMalloc, no allocating library routine); its first call on a device
+ * looks up that device's copy of the array.
+ *   Limit: parameters with rkv_workspace_bytes(p) > RKV_NOALLOC_WORKSPACE_BYTES
+ *   are rejected with RKV_ERR_WORKSPACE_TOO_SMALL (nothing launched).
+ *   Sharing: every call on one GPU uses that GPU's one array, and it keeps the
+ *   last call's contents (nothing in it needs to start at zero). Calls that
+ *   overlap on one GPU (other threads, other streams without ordering between
+ *   them) race on it: order them, or use rkv_evict_step with a workspace each.
+ * Errors: those of rkv_evict_step (without the workspace ones), plus
+ * RKV_ERR_HIP when the array's address cannot be obtained on the device.
+ */
+#define RKV_NOALLOC_WORKSPACE_BYTES (32u << 20)
+rkv_status rkv_evict_step_noalloc(const rkv_params* p, void* const* k_layers, void* const* v_layers,
+                                  const void* obs_q, int32_t* seq_start, int32_t* n_slots, void* stream);
 
 /* Static string naming a status. */
 const char* rkv_status_string(rkv_status st);

@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     RKV_MAX_CAPACITY,
     RKV_MAX_LAYERS,
     RKV_MAX_QROWS,
+    RKV_NOALLOC_WORKSPACE_BYTES,
     STATUS,
     RkvError,
     RkvParams,
@@ -29,6 +30,7 @@ from ._binding import (  # noqa: F401
     rkv_evict_step_sampled,
     rkv_evict_step_sentences,
     rkv_evict_step_captured,
+    rkv_evict_step_noalloc,
     rkv_decode_attention,
     rkv_evict_step_timed,
     rkv_last_hip_error,

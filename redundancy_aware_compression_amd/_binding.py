@@ -13,6 +13,7 @@ RKV_F32 = 1
 RKV_MAX_LAYERS = 128
 RKV_MAX_CAPACITY = 16384
 RKV_MAX_QROWS = 64
+RKV_NOALLOC_WORKSPACE_BYTES = 32 << 20
 
 STATUS = {
     0: "RKV_OK",
@@ -134,6 +135,8 @@ def _lib():
                                                vp, sz, vp]
         L.rkv_decode_attention.restype = ctypes.c_int
         L.rkv_decode_attention.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp]
+        L.rkv_evict_step_noalloc.restype = ctypes.c_int
+        L.rkv_evict_step_noalloc.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(i32), vp]
         L.rkv_evict_step_captured.restype = ctypes.c_int
         L.rkv_evict_step_captured.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(i32), vp, sz, vp]
         L.rkv_status_string.restype = ctypes.c_char_p
@@ -368,3 +371,15 @@ def rkv_evict_step_captured(p: RkvParams, k_layers: Sequence, v_layers: Sequence
         _check(st, "rkv_evict_step_captured")
     return st, ns.value
 
+
+def rkv_evict_step_noalloc(p: RkvParams, k_layers: Sequence, v_layers: Sequence, obs_q, seq_start, n_slots: int,
+                           stream=None, check: bool = True):
+    """rkv_evict_step on the library's built-in workspace (no allocation);
+    returns (status, n_slots after the step)."""
+    ns = ctypes.c_int32(n_slots)
+    st = _lib().rkv_evict_step_noalloc(ctypes.byref(p), _layers(p, k_layers, "k_layers"),
+                                       _layers(p, v_layers, "v_layers"), _ptr(obs_q), _ptr(seq_start),
+                                       ctypes.byref(ns), _stream(stream))
+    if check:
+        _check(st, "rkv_evict_step_noalloc")
+    return st, ns.value

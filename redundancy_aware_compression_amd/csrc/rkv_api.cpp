@@ -183,12 +183,13 @@ rkv_status check_sentences(const SentenceArgs& a) {
 rkv_status evict_impl(const rkv_params* p, void* const* k_layers, void* const* v_layers, const void* obs_q,
                       int32_t* seq_start, int32_t* order, bool holefill, int32_t* n_slots, void* ws, size_t ws_bytes,
                       void* stream, void* const* stage_events, const SentenceArgs* sent = nullptr,
-                      const float* imp_acc = nullptr) {
+                      const float* imp_acc = nullptr, bool builtin_ws = false) {
   rkv_status st = check_params(p);
   if (st != RKV_OK) return st;
   if ((st = check_layers(p, (const void* const*)k_layers)) != RKV_OK) return st;
   if ((st = check_layers(p, (const void* const*)v_layers)) != RKV_OK) return st;
-  if ((!obs_q && !imp_acc) || !seq_start || !n_slots || !ws || (holefill && !order)) return RKV_ERR_NULL_ARG;
+  if ((!obs_q && !imp_acc) || !seq_start || !n_slots || (!ws && !builtin_ws) || (holefill && !order))
+    return RKV_ERR_NULL_ARG;
   if (holefill && rkv::holefill_lds_bytes(p->budget) > rkv::kHolefillMaxLds) return RKV_ERR_UNSUPPORTED;
   if (sent && (st = check_sentences(*sent)) != RKV_OK) return st;
   if (!aligned16(obs_q) || ((uintptr_t)ws & 255u) || ((uintptr_t)order & 3u) || ((uintptr_t)imp_acc & 3u))
@@ -199,6 +200,10 @@ rkv_status evict_impl(const rkv_params* p, void* const* k_layers, void* const* v
   if (ws_bytes < w.bytes) return RKV_ERR_WORKSPACE_TOO_SMALL;
   // R-KV compresses once budget + buffer slots are full; below that, no-op.
   if (ns < p->budget + p->buffer) return RKV_OK;
+  if (builtin_ws) {  // every argument is valid: only now is the device's built-in workspace looked up
+    RKV_TRY(rkv::scratch_workspace(&ws));
+    w = rkv::carve(*p, ws);
+  }
   const rkv::Geom g = make_geom(p, ns);
   const rkv::LayerPtrs kl = make_layers(p, (const void* const*)k_layers);
   const rkv::LayerPtrs vl = make_layers(p, (const void* const*)v_layers);
@@ -358,6 +363,12 @@ rkv_status rkv_decode_attention(const rkv_params* p, const void* const* k_layers
   RKV_TRY(rkv::launch_decode(g, p->dtype, make_layers(p, k_layers), make_layers(p, v_layers), q, seq_start, out,
                              imp_acc, stream));
   return RKV_OK;
+}
+
+rkv_status rkv_evict_step_noalloc(const rkv_params* p, void* const* k_layers, void* const* v_layers,
+                                  const void* obs_q, int32_t* seq_start, int32_t* n_slots, void* stream) {
+  return evict_impl(p, k_layers, v_layers, obs_q, seq_start, nullptr, false, n_slots, nullptr,
+                    rkv::kScratchBytes, stream, nullptr, nullptr, nullptr, true);
 }
 
 rkv_status rkv_evict_step_captured(const rkv_params* p, void* const* k_layers, void* const* v_layers,

@@ -104,4 +104,10 @@ int launch_compact_holefill(const Geom& g, int dtype, const LayerPtrs& k, const 
 int launch_compact(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const int32_t* keep,
                    int32_t* seq_start, void* stream);
 
+// The built-in workspace of rkv_evict_step_noalloc (rkv_scratch.hip): a
+// device array of kScratchBytes per GPU; *ws receives its address on the
+// current device (looked up once per device). Returns a hipError_t.
+constexpr size_t kScratchBytes = (size_t)RKV_NOALLOC_WORKSPACE_BYTES;
+int scratch_workspace(void** ws);
+
 }  // namespace rkv

@@ -337,6 +337,23 @@ def test_binding_checks_layer_lists():
                          check=False) == st_of("RKV_ERR_NULL_ARG")
 
 
+def test_noalloc_limits_and_noop():
+    """The allocation-free step rejects parameters whose workspace exceeds its
+    built-in array, and takes the no-op path below the trigger, both before
+    touching any device."""
+    big = P(num_layers=32, batch=32, num_kv_heads=8, capacity=1152, budget=1024)
+    assert rkv.rkv_workspace_bytes(big) > rkv.RKV_NOALLOC_WORKSPACE_BYTES
+    st, ns = rkv.rkv_evict_step_noalloc(big, layers(32), layers(32), FAKE, FAKE, 1152, stream=0, check=False)
+    assert st == st_of("RKV_ERR_WORKSPACE_TOO_SMALL") and ns == 1152
+    p = P()
+    assert rkv.rkv_workspace_bytes(p) <= rkv.RKV_NOALLOC_WORKSPACE_BYTES
+    st, ns = rkv.rkv_evict_step_noalloc(p, layers(), layers(), FAKE, FAKE, 383, stream=0, check=False)
+    assert st == 0 and ns == 383
+    st, _ = rkv.rkv_evict_step_noalloc(p, layers(), layers(), 0, FAKE, 384, stream=0, check=False)
+    assert st == st_of("RKV_ERR_NULL_ARG")
+    st, _ = rkv.rkv_evict_step_noalloc(p, layers(), layers(), FAKE + 4, FAKE, 384, stream=0, check=False)
+    assert st == st_of("RKV_ERR_MISALIGNED")
+
 
 def test_one_hip_runtime_whatever_the_import_order():
     """Loading librkv before torch is imported must not map a second HIP
