@@ -52,7 +52,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "redundancy_aware_compression_amd", "csrc")
 # sources (and build flags) that determine each kernel's machine code
 KERNEL_SOURCES = {
-    "gram": ["rkv_gram.hip", "rkv_device.hpp", "rkv_internal.hpp"],
+    "gram": ["rkv_gram.hip", "rkv_tiles.hpp", "rkv_device.hpp", "rkv_internal.hpp"],
     "select": ["rkv_select.hip", "rkv_device.hpp", "rkv_internal.hpp"],
     "compact": ["rkv_compact.hip", "rkv_device.hpp", "rkv_internal.hpp"],
 }

@@ -283,8 +283,6 @@ __global__ __launch_bounds__(kHoleThreads) void holefill_kernel(Geom g, LayerPtr
   if (l == 0 && h == 0 && tid == 0) seq_start[b] = nlead;
 }
 
-size_t holefill_lds_bytes(int budget) { return ((6 * (size_t)budget + 15) & ~(size_t)15) + 4 * (size_t)((budget + 31) / 32); }
-
 int launch_compact_holefill(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const int32_t* keep,
                             int32_t* order, int32_t* seq_start, void* stream) {
   const int slices = g.L * g.batch * g.H;

@@ -15,7 +15,6 @@ namespace rkv {
 // Work-groups of 512 threads, or 256 where the weights leave room in LDS for
 // three of them per compute unit (short slices) and there are slices enough
 // for several per unit: more waves per unit then.
-constexpr int kDecMaxWaves = 8;
 constexpr size_t kDecSmallLds = 40 * 1024;
 
 // A lane holds one 16-byte chunk of a row: LPR lanes cover a row, RPI rows
@@ -337,11 +336,6 @@ __global__ __launch_bounds__(NT) void decode_kernel(Geom g, LayerPtrs k, LayerPt
     for (int w = 0; w < NW; ++w) s += lw[w * G * kHeadDim + e];
     o_out[e] = s * pick<G>(inv, e / kHeadDim);
   }
-}
-
-size_t decode_lds_bytes(int group, int n_slots) {
-  const int rows = n_slots > kDecMaxWaves * kHeadDim ? n_slots : kDecMaxWaves * kHeadDim;
-  return (size_t)group * rows * 4;
 }
 
 template <typename T, int G, int NT>

@@ -93,11 +93,19 @@ constexpr int kSentMaxDim = 8192;
 // KV head up to kDecMaxG; dynamic LDS of decode_lds_bytes(G, n_slots) bytes.
 int launch_decode(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const void* q,
                   const int32_t* seq_start, float* out, float* acc, void* stream);
-size_t decode_lds_bytes(int group, int n_slots);
+constexpr int kDecMaxWaves = 8;
+// the weights of every query head over max(n_slots, kDecMaxWaves * 128) rows, fp32
+inline size_t decode_lds_bytes(int group, int n_slots) {
+  const int rows = n_slots > kDecMaxWaves * kHeadDim ? n_slots : kDecMaxWaves * kHeadDim;
+  return (size_t)group * rows * 4;
+}
 constexpr int kDecMaxG = 8;
 constexpr size_t kDecMaxLds = 160 * 1024 - 1024;
 // dynamic LDS of the hole-filling compaction; launches keep it within 64 KB
-size_t holefill_lds_bytes(int budget);
+// three uint16 tables of budget entries (16-byte aligned) and one bit per row
+inline size_t holefill_lds_bytes(int budget) {
+  return ((6 * (size_t)budget + 15) & ~(size_t)15) + 4 * (size_t)((budget + 31) / 32);
+}
 constexpr size_t kHolefillMaxLds = 65536 - 2048;
 int launch_compact_holefill(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const int32_t* keep,
                             int32_t* order, int32_t* seq_start, void* stream);
