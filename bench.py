@@ -246,6 +246,11 @@ def kernel_table(w, ev_lens, moved, means, holefill=False, peaks=None):
             if mp:
                 k["measured_peak"] = mp
                 k["frac_measured_peak"] = k["achieved"] / mp
+            mr = peaks["peaks"].get("mfma_bf16_random_tflops") if k["unit"] == "TFLOP/s" and w.dtype == "bf16" \
+                else None
+            if mr:  # the matrix units' rate on operands as varied as real keys
+                k["measured_peak_random_operands"] = mr
+                k["frac_measured_peak_random_operands"] = k["achieved"] / mr
         if not (holefill and name == "compact"):  # rocprofv3 FETCH_SIZE + WRITE_SIZE, when summarised
             k["traffic"] = measured_traffic(name, w.name)
     if not holefill:  # the same fraction from counters: MFMA busy cycles over all SIMDs' cycles
@@ -263,6 +268,9 @@ def kernel_table(w, ev_lens, moved, means, holefill=False, peaks=None):
     if dk.get("frac_measured_peak") is not None:
         roofline["measured_peak"] = dk["measured_peak"]
         roofline["frac_measured_peak"] = dk["frac_measured_peak"]
+    if dk.get("frac_measured_peak_random_operands") is not None:
+        roofline["measured_peak_random_operands"] = dk["measured_peak_random_operands"]
+        roofline["frac_measured_peak_random_operands"] = dk["frac_measured_peak_random_operands"]
     return kernels, roofline
 
 
@@ -612,6 +620,7 @@ def measure_peaks(reps: int = 5):
 
     lib = load_hip_library(rkv_build.PEAKS_LIB_PATH)
     lib.rkv_peak_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.rkv_peak_mfma_bf16_random.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     lib.rkv_peak_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_void_p]
     lib.rkv_peak_hbm_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
@@ -649,6 +658,8 @@ def measure_peaks(reps: int = 5):
                 raise RuntimeError(f"{what}: hipError {rc}")
 
         mfma_ms = best_ms(lambda: check(lib.rkv_peak_mfma_bf16(blocks, iters, out.data_ptr(), sp), "mfma"))
+        mfma_rand_ms = best_ms(lambda: check(lib.rkv_peak_mfma_bf16_random(blocks, iters, out.data_ptr(), sp),
+                                             "mfma random"))
         read_ms = best_ms(lambda: check(lib.rkv_peak_hbm_read(buf.data_ptr(), read_bytes, hbm_blocks, red.data_ptr(),
                                                               sp), "read"))
         copy_ms = best_ms(lambda: check(lib.rkv_peak_hbm_copy(buf.data_ptr(), dst.data_ptr(), copy_bytes, hbm_blocks,
@@ -657,17 +668,22 @@ def measure_peaks(reps: int = 5):
     line = {
         "peaks": {
             "mfma_bf16_tflops": flops / (mfma_ms * 1e-3) / 1e12,
+            "mfma_bf16_random_tflops": flops / (mfma_rand_ms * 1e-3) / 1e12,
             "hbm_read_gbs": read_bytes / (read_ms * 1e-3) / 1e9,
             "hbm_copy_gbs": 2 * copy_bytes / (copy_ms * 1e-3) / 1e9,
         },
         "published": {"mfma_bf16_tflops": BF16_PEAK_TFLOPS, "hbm_gbs": HBM_PEAK_GBS},
-        "config": {"mfma": f"{blocks} work-groups x {tpb // 64} waves x {iters} rounds x 4 MFMA 32x32x16 bf16",
+        "config": {"mfma": f"{blocks} work-groups x {tpb // 64} waves x {iters} rounds x 4 MFMA 32x32x16 bf16; "
+                           "mfma_bf16_tflops on repetitive small operands, mfma_bf16_random_tflops on operands of "
+                           "random sign, exponent and mantissa (the matrix units' power, hence the clock, depends "
+                           "on the operand bits)",
                    "hbm": f"{hbm_blocks} work-groups x {tpb} threads over 32 KiB tiles, 8 non-temporal 16-byte loads "
                           "in flight per thread",
                    "hbm_read_bytes": read_bytes, "hbm_copy_bytes": copy_bytes, "best_of": reps},
     }
     line["fraction_of_published"] = {
         "mfma_bf16": line["peaks"]["mfma_bf16_tflops"] / BF16_PEAK_TFLOPS,
+        "mfma_bf16_random": line["peaks"]["mfma_bf16_random_tflops"] / BF16_PEAK_TFLOPS,
         "hbm_read": line["peaks"]["hbm_read_gbs"] / HBM_PEAK_GBS,
         "hbm_copy": line["peaks"]["hbm_copy_gbs"] / HBM_PEAK_GBS,
     }

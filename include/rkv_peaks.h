@@ -21,6 +21,11 @@ extern "C" {
  * each). out: float [blocks * rkv_peak_threads_per_block()], written. */
 int rkv_peak_mfma_bf16(int32_t blocks, int32_t iters, float* out, void* stream);
 
+/* The same with operands of random sign, exponent and mantissa (as keys drawn
+ * from N(0, 1) have): the matrix units then draw more power and the chip
+ * clocks lower, so this is the rate reachable on real keys. */
+int rkv_peak_mfma_bf16_random(int32_t blocks, int32_t iters, float* out, void* stream);
+
 /* Reads `bytes` (a multiple of 16, 16-byte aligned) of src with `blocks`
  * work-groups; out: uint32 [blocks], a fold of what was read. */
 int rkv_peak_hbm_read(const void* src, size_t bytes, int32_t blocks, uint32_t* out, void* stream);

@@ -79,6 +79,18 @@ rkv_status hip_status(int err) {
     if (st_ != RKV_OK) return st_;         \
   } while (0)
 
+// The scoring pass: the bf16 kernel (one work-group per slice, rkv_gram.hip)
+// or, for fp32 keys, the three-kernel pass of rkv_f32.hip on the workspace's
+// fp32 regions.
+int score(const rkv::Geom& g, int dtype, const rkv::LayerPtrs& k, const void* obs_q, const int32_t* seq_start,
+          const int32_t* order, const rkv::Workspace& w, float* importance, float* rowmean, int32_t* counts,
+          void* stream, const float* imp_acc) {
+  if (dtype == RKV_F32)
+    return rkv::launch_score_f32(g, k, obs_q, seq_start, order, w.f32_norms, w.f32_parts, importance, rowmean,
+                                 counts, stream, imp_acc);
+  return rkv::launch_gram(g, dtype, k, obs_q, seq_start, order, importance, rowmean, counts, stream, imp_acc);
+}
+
 }  // namespace
 
 extern "C" {
@@ -124,7 +136,7 @@ rkv_status rkv_score(const rkv_params* p, const void* const* k_layers, const voi
   const rkv::Geom g = make_geom(p, n_slots);
   const rkv::LayerPtrs kl = make_layers(p, k_layers);
   int32_t* cnt = counts ? counts : w.counts;
-  RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, nullptr, importance, w.rowmean, cnt, stream));
+  RKV_TRY(score(g, p->dtype, kl, obs_q, seq_start, nullptr, w, importance, w.rowmean, cnt, stream, nullptr));
   RKV_TRY(rkv::launch_redundancy(g, seq_start, cnt, w.rowmean, redundancy, stream));
   return RKV_OK;
 }
@@ -215,8 +227,8 @@ rkv_status evict_impl(const rkv_params* p, void* const* k_layers, void* const* v
   if (sent)
     RKV_TRY(rkv::launch_sentence_penalty(sent->vectors, sent->n_sent, p->batch, sent->s_max, sent->dim, sent->tau_s,
                                          sent->penalty, stream));
-  RKV_TRY(rkv::launch_gram(g, p->dtype, kl, obs_q, seq_start, holefill ? order : nullptr, w.importance, w.rowmean,
-                           w.counts, stream, imp_acc));
+  RKV_TRY(score(g, p->dtype, kl, obs_q, seq_start, holefill ? order : nullptr, w, w.importance, w.rowmean,
+                w.counts, stream, imp_acc));
   RKV_TRY(mark(1));
   RKV_TRY(rkv::launch_select(g, w.importance, nullptr, w.counts, w.rowmean, seq_start, w.keep, nullptr, nullptr,
                              stream, sent ? sent->penalty : nullptr, sent ? sent->sent_id : nullptr,

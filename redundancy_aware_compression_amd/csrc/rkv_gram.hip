@@ -840,21 +840,13 @@ int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q,
 #define RKV_GRAM(T, GA, CA)                                                                                   \
   RKV_LAUNCH((gram_kernel<T, GA, CA>), grid, block, 0, s, g, k, obs_q, seq_start, order, imp_acc, \
                      importance, rowmean, counts)
-  if (dtype == RKV_BF16) {
-    if (order)
-      RKV_GRAM(bf16_t, true, false);
-    else if (imp_acc)
-      RKV_GRAM(bf16_t, false, true);
-    else
-      RKV_GRAM(bf16_t, false, false);
-  } else {
-    if (order)
-      RKV_GRAM(float, true, false);
-    else if (imp_acc)
-      RKV_GRAM(float, false, true);
-    else
-      RKV_GRAM(float, false, false);
-  }
+  if (dtype != RKV_BF16) return (int)hipErrorInvalidValue;  // fp32 keys: launch_score_f32
+  if (order)
+    RKV_GRAM(bf16_t, true, false);
+  else if (imp_acc)
+    RKV_GRAM(bf16_t, false, true);
+  else
+    RKV_GRAM(bf16_t, false, false);
 #undef RKV_GRAM
   return 0;
 }

@@ -41,12 +41,22 @@ struct LayerPtrs {
 RKV_HD inline int gram_groups(int N) { return (N + kGroupBlocks * kRowBlock - 1) / (kGroupBlocks * kRowBlock); }
 RKV_HD inline int gram_row_blocks(int N, int g) { return (N + kRowBlock - 1) / kRowBlock - g * kGroupBlocks; }
 
+// The fp32 scoring pass (rkv_f32.hip) works in chunks of kF32Chunk keys;
+// each chunk leaves kF32PartFloats floats of partial statistics: the sum of
+// its unit keys (128), then per query row m the (max, sum of exp) of its
+// causal logits at 128 + 2 m.
+constexpr int kF32Chunk = 32;
+constexpr int kF32PartFloats = kHeadDim + 2 * RKV_MAX_QROWS;
+RKV_HD inline int f32_chunks(int n) { return (n + kF32Chunk - 1) / kF32Chunk; }
+
 // Workspace regions, each 256-byte aligned, sized for n_slots = capacity.
 struct Workspace {
   float* rowmean;     // [slices][n_slots]
   int32_t* counts;    // [slices][n_slots]
   float* importance;  // [slices][n_slots]
   int32_t* keep;      // [slices][budget]
+  float* f32_norms;   // fp32 keys only: [slices][n_slots] key norms
+  float* f32_parts;   // fp32 keys only: [slices][f32_chunks(capacity)][kF32PartFloats]
   size_t bytes;
 };
 
@@ -67,6 +77,11 @@ inline Workspace carve(const rkv_params& p, void* base) {
   w.counts = (int32_t*)take(slices * cap * 4);
   w.importance = (float*)take(slices * cap * 4);
   w.keep = (int32_t*)take(slices * (size_t)p.budget * 4);
+  w.f32_norms = w.f32_parts = nullptr;
+  if (p.dtype == RKV_F32) {
+    w.f32_norms = (float*)take(slices * cap * 4);
+    w.f32_parts = (float*)take(slices * (size_t)f32_chunks((int)cap) * kF32PartFloats * 4);
+  }
   w.bytes = off;
   return w;
 }
@@ -78,6 +93,14 @@ inline Workspace carve(const rkv_params& p, void* base) {
 int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q, const int32_t* seq_start,
                 const int32_t* order, float* importance, float* rowmean, int32_t* counts, void* stream,
                 const float* imp_acc = nullptr);
+// The scoring pass for fp32 keys (rkv_f32.hip): statistics per chunk of
+// keys, similar-pair counts per 32x32 tile of the upper triangle, then row
+// means and importance per token. Same inputs and outputs as launch_gram
+// (counts are accumulated: the first kernel clears them); norms and parts
+// are the workspace's fp32 regions.
+int launch_score_f32(const Geom& g, const LayerPtrs& k, const void* obs_q, const int32_t* seq_start,
+                     const int32_t* order, float* norms, float* parts, float* importance, float* rowmean,
+                     int32_t* counts, void* stream, const float* imp_acc);
 int launch_redundancy(const Geom& g, const int32_t* seq_start, const int32_t* counts, const float* rowmean,
                       float* redundancy, void* stream);
 int launch_select_sampled(const Geom& g, const float* scores, const float* uniforms, const int32_t* seq_start,

@@ -15,16 +15,41 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // Four independent 32x32x16 bf16 MFMA chains per wave, `iters` rounds: one
-// MFMA issue every time the matrix pipe of the SIMD is free. Operands come
-// from the lane id so the compiler cannot fold them; one float per lane is
-// written so the chains are not removed.
+// MFMA issue every time the matrix pipe of the SIMD is free. One float per
+// lane is written so the chains are not removed.
+//
+// The matrix units draw more power on operands whose bits change (signs,
+// exponents, mantissas) than on repetitive ones, and under that load the
+// chip lowers its clock. LOW: few distinct small values from the lane id,
+// which keeps the clock up and approaches the published rate. RANDOM: every
+// lane's 16 operands are bf16 values of random sign, exponent in [2^-2, 2^2)
+// and random mantissa (about what keys drawn from N(0, 1) look like), from a
+// xorshift generator seeded by lane and work-group: the rate a kernel on
+// real keys can reach at best.
+template <bool RANDOM>
 __global__ __launch_bounds__(kThreads) void mfma_peak_kernel(int iters, float* __restrict__ out) {
   const int tid = threadIdx.x;
   bf16x8 a, b;
+  uint32_t h = ((uint32_t)tid + 1u) * 2654435761u ^ ((uint32_t)blockIdx.x + 1u) * 40503u;
+  auto next = [&]() {
+    h ^= h << 13;
+    h ^= h >> 17;
+    h ^= h << 5;
+    return h;
+  };
+  auto rand_bf16 = [&]() {
+    const uint32_t r = next();
+    return __builtin_bit_cast(__bf16, (uint16_t)((r & 0x8000u) | ((125u + ((r >> 20) & 3u)) << 7) | (r & 0x7Fu)));
+  };
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    a[i] = (__bf16)(0.001f * (float)((tid + i) & 7));
-    b[i] = (__bf16)(0.002f * (float)((tid ^ i) & 7));
+    if constexpr (RANDOM) {
+      a[i] = rand_bf16();
+      b[i] = rand_bf16();
+    } else {
+      a[i] = (__bf16)(0.001f * (float)((tid + i) & 7));
+      b[i] = (__bf16)(0.002f * (float)((tid ^ i) & 7));
+    }
   }
   f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
   for (int it = 0; it < iters; ++it) {
@@ -96,7 +121,15 @@ extern "C" {
 int rkv_peak_mfma_bf16(int32_t blocks, int32_t iters, float* out, void* stream) {
   if (blocks < 1 || iters < 1 || !out) return (int)hipErrorInvalidValue;
   void* args[] = {&iters, &out};
-  return (int)hipLaunchKernel((const void*)mfma_peak_kernel, dim3(blocks), dim3(kThreads), args, 0, (hipStream_t)stream);
+  return (int)hipLaunchKernel((const void*)mfma_peak_kernel<false>, dim3(blocks), dim3(kThreads), args, 0,
+                              (hipStream_t)stream);
+}
+
+int rkv_peak_mfma_bf16_random(int32_t blocks, int32_t iters, float* out, void* stream) {
+  if (blocks < 1 || iters < 1 || !out) return (int)hipErrorInvalidValue;
+  void* args[] = {&iters, &out};
+  return (int)hipLaunchKernel((const void*)mfma_peak_kernel<true>, dim3(blocks), dim3(kThreads), args, 0,
+                              (hipStream_t)stream);
 }
 
 int rkv_peak_hbm_read(const void* src, size_t bytes, int32_t blocks, uint32_t* out, void* stream) {

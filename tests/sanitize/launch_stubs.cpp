@@ -19,6 +19,10 @@ int launch_gram(const Geom&, int, const LayerPtrs&, const void*, const int32_t*,
                 int32_t*, void*, const float*) {
   launched("launch_gram");
 }
+int launch_score_f32(const Geom&, const LayerPtrs&, const void*, const int32_t*, const int32_t*, float*, float*,
+                     float*, float*, int32_t*, void*, const float*) {
+  launched("launch_score_f32");
+}
 int launch_redundancy(const Geom&, const int32_t*, const int32_t*, const float*, float*, void*) {
   launched("launch_redundancy");
 }

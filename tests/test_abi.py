@@ -299,7 +299,7 @@ def test_peaks_library_exports_its_header():
 
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "rkv_peaks.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(rkv_peak_[a-z_0-9]+)\s*\(", text)))
-    assert {"rkv_peak_mfma_bf16", "rkv_peak_hbm_read", "rkv_peak_hbm_copy"} <= set(names)
+    assert {"rkv_peak_mfma_bf16", "rkv_peak_mfma_bf16_random", "rkv_peak_hbm_read", "rkv_peak_hbm_copy"} <= set(names)
     lib = load_hip_library(rkv_build.PEAKS_LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -311,6 +311,8 @@ def test_peaks_library_exports_its_header():
     assert lib.rkv_peak_hbm_read(FAKE, 100, 4, FAKE, None) != 0  # not a multiple of 16
     assert lib.rkv_peak_hbm_copy(FAKE + 8, FAKE, 4096, 4, None) != 0  # misaligned
     assert lib.rkv_peak_mfma_bf16(0, 10, FAKE, None) != 0  # no work-groups
+    lib.rkv_peak_mfma_bf16_random.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.rkv_peak_mfma_bf16_random(4, 0, FAKE, None) != 0  # no rounds
     assert lib.rkv_peak_threads_per_block() == 256
 
 
