@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Geom g, const fl
                                                                 float* __restrict__ r_out,
                                                                 const float* __restrict__ sent_pen,
                                                                 const int32_t* __restrict__ sent_id, int s_max) {
-  __shared__ uint32_t keys[RKV_MAX_CAPACITY];
+  extern __shared__ uint32_t keys[];  // dynamic: n_slots entries (select_lds_bytes)
   __shared__ __align__(16) int hist[2 * kHistInts];
   __shared__ float fscr[16];
   __shared__ int iscr[16];
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_sampled_kernel(Geom g, 
                                                                         const int32_t* __restrict__ seq_start,
                                                                         int keep_newest, int top_k, float inv_temp,
                                                                         int32_t* __restrict__ keep) {
-  __shared__ uint32_t keys[RKV_MAX_CAPACITY];
+  extern __shared__ uint32_t keys[];  // dynamic: n_slots entries (select_lds_bytes)
   __shared__ __align__(16) int hist[2 * kHistInts];
   __shared__ int iscr[16];
   __shared__ int sel[2];
@@ -402,12 +402,24 @@ __global__ __launch_bounds__(kSelectThreads) void select_sampled_kernel(Geom g, 
   }
 }
 
+// The keys of a slice's candidates live in dynamic LDS sized for n_slots, so
+// short slices leave room for more work-groups per compute unit.
+static size_t select_lds_bytes(const Geom& g) { return (size_t)(g.n_slots > 0 ? g.n_slots : 1) * 4; }
+
+// Allows `kernel` dynamic LDS beyond the default 64 KB when it needs it.
+static int allow_lds(const void* kernel, size_t lds) {
+  if (lds <= 48 * 1024) return 0;
+  return (int)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
 int launch_select_sampled(const Geom& g, const float* scores, const float* uniforms, const int32_t* seq_start,
                           int keep_newest, int top_k, float temperature, int32_t* keep, void* stream) {
   const int slices = g.L * g.batch * g.H;
   if (slices == 0) return 0;
-  RKV_LAUNCH(select_sampled_kernel, dim3(slices), dim3(kSelectThreads), 0, (hipStream_t)stream, g, scores,
-                     uniforms, seq_start, keep_newest, top_k, 1.f / temperature, keep);
+  const size_t lds = select_lds_bytes(g);
+  if (const int e = allow_lds((const void*)select_sampled_kernel, lds)) return e;
+  RKV_LAUNCH(select_sampled_kernel, dim3(slices), dim3(kSelectThreads), lds, (hipStream_t)stream, g, scores,
+             uniforms, seq_start, keep_newest, top_k, 1.f / temperature, keep);
   return 0;
 }
 
@@ -418,15 +430,20 @@ int launch_select(const Geom& g, const float* importance, const float* redundanc
   if (slices == 0) return 0;
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid(slices), block(kSelectThreads);
+  const size_t lds = select_lds_bytes(g);
+#define RKV_SELECT(FC, PEN)                                                                              \
+  do {                                                                                                   \
+    if (const int e = allow_lds((const void*)select_kernel<FC, PEN>, lds)) return e;                     \
+    RKV_LAUNCH((select_kernel<FC, PEN>), grid, block, lds, s, g, importance, redundancy, counts, rowmean, \
+               seq_start, keep, z_out, r_out, sent_pen, sent_id, s_max);                                 \
+  } while (0)
   if (counts && sent_pen)
-    RKV_LAUNCH((select_kernel<true, true>), grid, block, 0, s, g, importance, redundancy, counts, rowmean,
-                       seq_start, keep, z_out, r_out, sent_pen, sent_id, s_max);
+    RKV_SELECT(true, true);
   else if (counts)
-    RKV_LAUNCH((select_kernel<true, false>), grid, block, 0, s, g, importance, redundancy, counts, rowmean,
-                       seq_start, keep, z_out, r_out, sent_pen, sent_id, s_max);
+    RKV_SELECT(true, false);
   else
-    RKV_LAUNCH((select_kernel<false, false>), grid, block, 0, s, g, importance, redundancy, counts,
-                       rowmean, seq_start, keep, z_out, r_out, sent_pen, sent_id, s_max);
+    RKV_SELECT(false, false);
+#undef RKV_SELECT
   return 0;
 }
 
