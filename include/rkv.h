@@ -46,6 +46,16 @@
  *   seq_start into range so a violation never addresses memory outside the
  *   caller's buffers, but the result is then unspecified. No entry point
  *   prints, aborts or throws.
+ *   Debug checks. When the environment variable RKV_DEBUG holds a non-zero
+ *   integer at the time of a call, rkv_score and every rkv_evict_step*
+ *   entry point that would launch work first check those preconditions on
+ *   the device: every seq_start[b] within [0, n_slots]; every key and value
+ *   element of the valid slots and every observation-query element finite
+ *   (those the call reads); with the hole-filling layout, each slice's order
+ *   a permutation of [0, budget). They then synchronise `stream` and, on a
+ *   violation, return RKV_ERR_PRECONDITION with nothing else launched and
+ *   nothing written but the workspace. Off by default; benchmarks leave it
+ *   off.
  */
 #ifndef RKV_H
 #define RKV_H
@@ -65,7 +75,8 @@ typedef enum {
   RKV_ERR_WORKSPACE_TOO_SMALL = 4, /* ws_bytes < rkv_workspace_bytes(p)               */
   RKV_ERR_MISALIGNED = 5,          /* a tensor pointer is not 16-byte aligned         */
   RKV_ERR_UNSUPPORTED = 6,         /* valid but not implemented (e.g. head_dim != 128) */
-  RKV_ERR_HIP = 7                  /* a HIP launch failed                             */
+  RKV_ERR_HIP = 7,                 /* a HIP launch failed                             */
+  RKV_ERR_PRECONDITION = 8         /* RKV_DEBUG: a device-data precondition failed    */
 } rkv_status;
 
 typedef enum { RKV_BF16 = 0, RKV_F32 = 1 } rkv_dtype;

@@ -24,6 +24,7 @@ STATUS = {
     5: "RKV_ERR_MISALIGNED",
     6: "RKV_ERR_UNSUPPORTED",
     7: "RKV_ERR_HIP",
+    8: "RKV_ERR_PRECONDITION",
 }
 
 

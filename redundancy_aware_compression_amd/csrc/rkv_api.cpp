@@ -3,6 +3,7 @@
 // error path leaves device memory untouched and needs no GPU.
 #include <hip/hip_runtime_api.h>
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "rkv.h"
@@ -91,6 +92,26 @@ int score(const rkv::Geom& g, int dtype, const rkv::LayerPtrs& k, const void* ob
   return rkv::launch_gram(g, dtype, k, obs_q, seq_start, order, importance, rowmean, counts, stream, imp_acc);
 }
 
+// RKV_DEBUG: a non-zero integer in the environment variable at the time of
+// the call turns the device precondition checks on.
+bool debug_checks() {
+  const char* e = getenv("RKV_DEBUG");
+  return e && atoi(e) != 0;
+}
+
+// The checks of rkv_debug.hip on the step's inputs, then a sync of the
+// stream and the violation bits read back: RKV_ERR_PRECONDITION when any is
+// set. vl.p[0] == NULL: no values to check.
+rkv_status debug_check(const rkv::Geom& g, int dtype, const rkv::LayerPtrs& kl, const rkv::LayerPtrs& vl,
+                       const void* obs_q, const int32_t* seq_start, const int32_t* order, const rkv::Workspace& w,
+                       void* stream) {
+  RKV_TRY(rkv::launch_debug_check(g, dtype, kl, vl, obs_q, seq_start, order, w.flags, stream));
+  RKV_TRY((int)hipStreamSynchronize((hipStream_t)stream));
+  uint32_t bits = 0u;
+  RKV_TRY((int)hipMemcpy(&bits, w.flags, sizeof(bits), hipMemcpyDeviceToHost));
+  return bits ? RKV_ERR_PRECONDITION : RKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -115,6 +136,7 @@ const char* rkv_status_string(rkv_status st) {
     case RKV_ERR_MISALIGNED: return "RKV_ERR_MISALIGNED";
     case RKV_ERR_UNSUPPORTED: return "RKV_ERR_UNSUPPORTED";
     case RKV_ERR_HIP: return "RKV_ERR_HIP";
+    case RKV_ERR_PRECONDITION: return "RKV_ERR_PRECONDITION";
   }
   return "RKV_ERR_UNKNOWN";
 }
@@ -135,6 +157,11 @@ rkv_status rkv_score(const rkv_params* p, const void* const* k_layers, const voi
   if (n_slots <= p->budget) return RKV_OK;  // no sequence can exceed the budget
   const rkv::Geom g = make_geom(p, n_slots);
   const rkv::LayerPtrs kl = make_layers(p, k_layers);
+  if (debug_checks()) {
+    rkv::LayerPtrs none;
+    memset(&none, 0, sizeof(none));
+    if ((st = debug_check(g, p->dtype, kl, none, obs_q, seq_start, nullptr, w, stream)) != RKV_OK) return st;
+  }
   int32_t* cnt = counts ? counts : w.counts;
   RKV_TRY(score(g, p->dtype, kl, obs_q, seq_start, nullptr, w, importance, w.rowmean, cnt, stream, nullptr));
   RKV_TRY(rkv::launch_redundancy(g, seq_start, cnt, w.rowmean, redundancy, stream));
@@ -219,6 +246,9 @@ rkv_status evict_impl(const rkv_params* p, void* const* k_layers, void* const* v
   const rkv::Geom g = make_geom(p, ns);
   const rkv::LayerPtrs kl = make_layers(p, (const void* const*)k_layers);
   const rkv::LayerPtrs vl = make_layers(p, (const void* const*)v_layers);
+  if (debug_checks() &&
+      (st = debug_check(g, p->dtype, kl, vl, obs_q, seq_start, holefill ? order : nullptr, w, stream)) != RKV_OK)
+    return st;
   auto mark = [&](int i) -> int {
     if (!stage_events || !stage_events[i]) return 0;
     return (int)hipEventRecord((hipEvent_t)stage_events[i], (hipStream_t)stream);
@@ -331,6 +361,11 @@ rkv_status rkv_evict_step_sampled(const rkv_params* p, void* const* k_layers, vo
   if (ws_bytes < w.bytes) return RKV_ERR_WORKSPACE_TOO_SMALL;
   if (ns < p->budget + p->buffer) return RKV_OK;  // below the trigger: no-op
   const rkv::Geom g = make_geom(p, ns);
+  if (debug_checks() &&
+      (st = debug_check(g, p->dtype, make_layers(p, (const void* const*)k_layers),
+                        make_layers(p, (const void* const*)v_layers), nullptr, seq_start, nullptr, w, stream)) !=
+          RKV_OK)
+    return st;
   RKV_TRY(rkv::launch_select_sampled(g, scores, uniforms, seq_start, keep_newest, top_k, temperature, w.keep,
                                      stream));
   RKV_TRY(rkv::launch_compact(g, p->dtype, make_layers(p, (const void* const*)k_layers),

@@ -55,6 +55,7 @@ struct Workspace {
   int32_t* counts;    // [slices][n_slots]
   float* importance;  // [slices][n_slots]
   int32_t* keep;      // [slices][budget]
+  uint32_t* flags;    // 64 words: the RKV_DEBUG checks' violation bits (word 0)
   float* f32_norms;   // fp32 keys only: [slices][n_slots] key norms
   float* f32_parts;   // fp32 keys only: [slices][f32_chunks(capacity)][kF32PartFloats]
   size_t bytes;
@@ -77,6 +78,7 @@ inline Workspace carve(const rkv_params& p, void* base) {
   w.counts = (int32_t*)take(slices * cap * 4);
   w.importance = (float*)take(slices * cap * 4);
   w.keep = (int32_t*)take(slices * (size_t)p.budget * 4);
+  w.flags = (uint32_t*)take(256);
   w.f32_norms = w.f32_parts = nullptr;
   if (p.dtype == RKV_F32) {
     w.f32_norms = (float*)take(slices * cap * 4);
@@ -134,6 +136,15 @@ int launch_compact_holefill(const Geom& g, int dtype, const LayerPtrs& k, const 
                             int32_t* order, int32_t* seq_start, void* stream);
 int launch_compact(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const int32_t* keep,
                    int32_t* seq_start, void* stream);
+
+// RKV_DEBUG device checks (rkv_debug.hip): clears flags[0], then ORs into
+// it kDbgSeqStart when some seq_start[b] lies outside [0, n_slots],
+// kDbgKV when a key or value element of a valid slot is not finite, kDbgQuery
+// when an element of obs_q (if given) is not finite, kDbgOrder when order (if
+// given) is not a permutation of [0, budget) for some slice.
+constexpr uint32_t kDbgSeqStart = 1, kDbgKV = 2, kDbgQuery = 4, kDbgOrder = 8;
+int launch_debug_check(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const void* obs_q,
+                       const int32_t* seq_start, const int32_t* order, uint32_t* flags, void* stream);
 
 // The built-in workspace of rkv_evict_step_noalloc (rkv_scratch.hip): a
 // device array of kScratchBytes per GPU; *ws receives its address on the

@@ -48,5 +48,9 @@ int launch_compact_holefill(const Geom&, int, const LayerPtrs&, const LayerPtrs&
 int launch_compact(const Geom&, int, const LayerPtrs&, const LayerPtrs&, const int32_t*, int32_t*, void*) {
   launched("launch_compact");
 }
+int launch_debug_check(const Geom&, int, const LayerPtrs&, const LayerPtrs&, const void*, const int32_t*,
+                       const int32_t*, uint32_t*, void*) {
+  launched("launch_debug_check");
+}
 int scratch_workspace(void**) { launched("scratch_workspace"); }
 }  // namespace rkv
