@@ -60,14 +60,16 @@ static_assert(RKV_MAX_QROWS <= kRowBlock, "the query rows fill one stage-sized r
 static_assert(kRowBlock == 8 * kGramWaves, "pre-pass: 8 lanes per row, 8 rows per wave");
 
 
+// bf16 keys only: fp32 keys take the scoring pass of rkv_f32.hip.
 template <typename T>
 struct Stage {
-  static constexpr int RB = kHeadDim * Elem<T>::kBytes;      // bytes per key row
-  static constexpr int SLOTS = RB / 16;                       // 16-byte slots per row
-  static constexpr int BYTES = kRowBlock * RB;                // one row block
-  static constexpr int PER = BYTES / 1024 / kGramWaves;       // 1 KB direct loads per wave per row block
-  static constexpr int COUNT = sizeof(T) == 2 ? 7 : 3;        // ring depth (LDS: ring + queries + norms <= 160 KB)
-  static constexpr int NCACHE = sizeof(T) == 2 ? 5120 : 1024; // tokens whose norms stay in LDS after group 0
+  static_assert(sizeof(T) == 2, "the Gram kernel takes bf16 keys");
+  static constexpr int RB = kHeadDim * Elem<T>::kBytes;  // bytes per key row
+  static constexpr int SLOTS = RB / 16;                   // 16-byte slots per row
+  static constexpr int BYTES = kRowBlock * RB;            // one row block
+  static constexpr int PER = BYTES / 1024 / kGramWaves;   // 1 KB direct loads per wave per row block
+  static constexpr int COUNT = 7;                         // ring depth (LDS: ring + queries + norms <= 160 KB)
+  static constexpr int NCACHE = 5120;                     // tokens whose norms stay in LDS after group 0
   static_assert(kRowBlock % kGramWaves == 0 && BYTES % (1024 * kGramWaves) == 0, "row block split");
   static_assert(COUNT >= 3 && COUNT <= 8, "ring depth");
 };
@@ -102,9 +104,9 @@ __device__ inline void issue_rows(uint32_t st_rows, u32x4_t r, const uint32_t* v
   for (int q = 0; q < S::PER; ++q) dma_to_lds16(r, st_rows + (wave * S::PER + q) * 1024, voff[q], soff);
 }
 
-// 16x16 logit tiles: lane l supplies row (l % 16) of a tile and, per MFMA,
-// the 8 (bf16, 16x16x32) or 1 (fp32, 16x16x4) dims of its quarter l / 16;
-// the result holds column l % 16 and rows 4 (l / 16) + r in register r.
+// 16x16 logit tiles: lane l supplies row (l % 16) of a tile and, per
+// 16x16x32 MFMA, 8 dims of its quarter l / 16; the result holds column
+// l % 16 and rows 4 (l / 16) + r in register r.
 template <typename T>
 struct Tile16;
 template <>
@@ -125,23 +127,6 @@ struct Tile16<bf16_t> {
                                                     __builtin_bit_cast(bf16x8_t, b.v[s]), acc, 0, 0, 0);
   }
 };
-template <>
-struct Tile16<float> {
-  struct F {
-    float v[32];  // dim 4 s + quarter
-  };
-  __device__ static void load(F& f, const char* st_rows, int R, int quarter) {
-    const char* row = st_rows + R * (kHeadDim * 4);
-    const int sw = R & 15;
-#pragma unroll
-    for (int s = 0; s < 32; ++s) f.v[s] = *(const float*)(row + ((s ^ sw) * 16) + quarter * 4);
-  }
-  __device__ static void mma(f32x4& acc, const F& a, const F& b) {
-#pragma unroll
-    for (int s = 0; s < 32; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], acc, 0, 0, 0);
-  }
-};
-
 // 16 consecutive dims [16 c, +16) of staged row R as fp32 (exact widening).
 template <typename T>
 __device__ inline void row_chunk16(float* x, const char* st_rows, int R, int c) {
@@ -155,12 +140,8 @@ __device__ inline void row_chunk16(float* x, const char* st_rows, int R, int c) 
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (sizeof(T) == 2) {
-        x[u * 8 + 2 * e] = __uint_as_float(w[e] << 16);
-        x[u * 8 + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-      } else {
-        x[u * 4 + e] = __uint_as_float(w[e]);
-      }
+      x[u * 8 + 2 * e] = __uint_as_float(w[e] << 16);
+      x[u * 8 + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
     }
   }
 }
@@ -502,15 +483,14 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
         }
       }
       uint32_t bits[2] = {0u, 0u};  // sign bits of the block's 32 rows per column fragment
-      if (sizeof(T) == 2 && __builtin_expect(!diag, 1)) {
+      if (__builtin_expect(!diag, 1)) {
         // Both 32-row halves' products first, then the first half's epilogue
         // placed between the second half's 16 MFMAs (4 VALU after each): the
-        // epilogue runs in the matrix units' shadow. (With fp32 keys the extra
-        // accumulators would not fit in registers. With GATHER they take the
-        // last registers and the compiler spills 8 bytes; spill traffic only
-        // adds vector memory operations younger than the rows a wait is for,
-        // and loads return in order, so every computed vmcnt wait stays
-        // sufficient.)
+        // epilogue runs in the matrix units' shadow. (With GATHER the extra
+        // accumulators take the last registers and the compiler spills 8
+        // bytes; spill traffic only adds vector memory operations younger
+        // than the rows a wait is for, and loads return in order, so every
+        // computed vmcnt wait stays sufficient.)
         float nj0[16], nj1[16];
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
