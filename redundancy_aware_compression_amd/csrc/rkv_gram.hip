@@ -17,10 +17,11 @@
 // (64 tokens each), wave w holding block 8g+w as MFMA B fragments in
 // registers; it meets every row block of newer tokens from 8g to the end of
 // the slice. All groups' row blocks form one stream through an LDS ring
-// (8 stages of 16 KB) filled by direct buffer-to-LDS loads (no staging
-// registers, hardware range checks past the slice); a stage is refilled as
-// soon as every wave is past it, so the ring prefetches across group
-// boundaries. LDS rows are XOR-swizzled in 16-byte slots so the MFMA operand
+// (7 stages of 16 KB) filled by direct buffer-to-LDS loads (no staging
+// registers, hardware range checks past the slice). One barrier covers two
+// blocks of the stream; a wave refills a stage right after its Gram work on
+// a block once every wave is past the stage, so the refills spread over the
+// iteration and the ring prefetches across group boundaries. LDS rows are XOR-swizzled in 16-byte slots so the MFMA operand
 // reads are conflict-free. A wave has nothing to do before its own block; it
 // takes its columns from the ring there (no separate column loads), so about
 // the upper triangle j >= i is computed.
@@ -432,36 +433,64 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   using First = std::integral_constant<bool, true>;
   using Later = std::integral_constant<bool, false>;
 
-  // block 0 (and the queries) landed, then its norms and statistics
-  // block 0 and the queries (issued after ROW(0), before ROW(1))
+  // Stream blocks per barrier: the pre-pass runs BPB blocks ahead of the
+  // Gram work, so one barrier covers BPB blocks (their norms written by other
+  // waves, the next BPB blocks landed, the stages of the previous BPB free).
+  // The ring holds BPB blocks in Gram work, BPB in the pre-pass and at least
+  // BPB in flight. The gathered stream keeps one block per barrier (its
+  // order-table loads are counted per refill).
+  constexpr int BPB = GATHER ? 1 : 2;
+  static_assert(S::COUNT >= 3 * BPB, "ring depth for the blocks per barrier");
+  auto pre_any = [&](int x) {
+    if (x < nrb)
+      pre(x, First{});
+    else
+      pre(x, Later{});
+  };
+
+  // blocks 0 .. BPB - 1 and the queries (issued after ROW(0), before ROW(1))
   if constexpr (GATHER)
     wait_vm(pro_n == 1 ? 0 : end_row(pro_n - 1) - 2 * S::PER - o0);
   else
-    wait_later_blocks<S::PER>(pro_n - 1);
+    wait_later_blocks<S::PER>(pro_n - min(BPB, pro_n));
   __syncthreads();
-  pre(0, First{});
+#pragma unroll 1
+  for (int x = 0; x < BPB && x < total; ++x) pre_any(x);
 
   Frag<T> bf[2];  // this group's column keys of the wave: fragment f holds columns cbase + 32 f + (0..31)
   float tn[2] = {0.f, 0.f}, nrm_i[2] = {0.f, 0.f};
   uint32_t cnt[2] = {0u, 0u};
 
-  // the start of stream iteration q: block q + 1 must have landed for its
-  // pre-pass. Blocks issued so far: the first COUNT, then one refill per
-  // iteration from iteration 1 on (block q' - 1 + COUNT in iteration q'), the
-  // last before this wait being max(COUNT - 1, q + COUNT - 2)
+  // the start of stream iteration q (a multiple of BPB): blocks q + BPB ..
+  // q + 2 BPB - 1 must have landed for their pre-pass. Blocks issued so far:
+  // the first COUNT, then one refill per block (BPB = 1: block q' - 1 + COUNT
+  // at iteration q' >= 1, after its barrier; BPB = 2: block q' - 2 + COUNT
+  // after Gram block q' >= 2), the last before this wait being
+  // max(COUNT - 1, q - 1 - BPB + COUNT)
   auto advance = [&](int q) {
-    const int X = q - 1 + S::COUNT;  // the refill's block
-    const bool refill = q >= 1 && X < total;
-    if (q + 1 < total) {
-      const int last = min(total - 1, max(S::COUNT - 1, q + S::COUNT - 2));
+    if (q + BPB < total) {
+      const int last = min(total - 1, max(S::COUNT - 1, q - 1 - BPB + S::COUNT));
+      const int need = min(total - 1, q + 2 * BPB - 1);
       if constexpr (GATHER)
-        wait_vm(end_row(last) - end_row(q + 1));
+        wait_vm(end_row(last) - end_row(need));
       else
-        wait_later_blocks<S::PER>(last - (q + 1));
+        wait_later_blocks<S::PER>(last - need);
     }
-    __syncthreads();  // block q's norms are in LDS, block q + 1 has landed, and
-                      // every wave is done with block q - 1, whose stage is free
-    if (refill) issue_next(X);
+    __syncthreads();  // the norms of blocks q .. q + BPB - 1 are in LDS, the
+                      // next BPB blocks have landed, and every wave is done
+                      // with blocks q - BPB .. q - 1, whose stages are free
+    if (BPB == 1) {
+      const int X = q - 1 + S::COUNT;
+      if (X >= S::COUNT && X < total) issue_next(X);
+    }
+  };
+  // BPB = 2: after Gram block q, the refill of the stage of block q - 2
+  // (every wave passed the barrier at the start of q's iteration after
+  // finishing q - 2), issued here rather than all at the barrier so that the
+  // waves' loads do not queue up together
+  auto refill2 = [&](int q) {
+    const int X = q - 2 + S::COUNT;
+    if (BPB == 2 && X >= S::COUNT && X < total) issue_next(X);
   };
 
   // Gram work of stream block q = block bi of group gg
@@ -487,7 +516,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
         // Both 32-row halves' products first, then the first half's epilogue
         // placed between the second half's 16 MFMAs (4 VALU after each): the
         // epilogue runs in the matrix units' shadow. (With GATHER the extra
-        // accumulators take the last registers and the compiler spills 8
+        // accumulators take the last registers and the compiler spills 16
         // bytes; spill traffic only adds vector memory operations younger
         // than the rows a wait is for, and loads return in order, so every
         // computed vmcnt wait stays sufficient.)
@@ -771,14 +800,26 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
     cnt[0] = cnt[1] = 0u;
   };
 
-  // group 0, with the statistics pre-pass over every key of the slice
+  // The stream: group 0 (with the statistics pre-pass over every key of the
+  // slice), then the later groups; after a group's last block its epilogue
+  // (after group 0 the statistics merge first). The barrier and the pre-pass
+  // come every BPB blocks; a pair of blocks may straddle a group's end.
+  auto step = [&](int q, auto first) {
+    if (q % BPB == 0) {
+      advance(q);
+#pragma unroll 1
+      for (int x = q + BPB; x < q + 2 * BPB && x < total; ++x) {
+        if constexpr (decltype(first)::value)
+          pre_any(x);
+        else
+          pre(x, Later{});
+      }
+    }
+  };
   for (int q = 0; q < nrb; ++q) {
-    advance(q);
-    if (q + 1 < nrb)
-      pre(q + 1, First{});
-    else if (q + 1 < total)
-      pre(q + 1, Later{});
+    step(q, First{});
     gram_block(q, 0, q);
+    refill2(q);
   }
   merge_stats();
   epilogue(0);
@@ -787,9 +828,9 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   for (int gg = 1; gg < ngroups; ++gg) {
     const int nbg = nrb - gg * kGroupBlocks;  // row blocks of this group
     for (int bi = 0; bi < nbg; ++bi, ++q) {
-      advance(q);
-      if (q + 1 < total) pre(q + 1, Later{});
+      step(q, Later{});
       gram_block(q, gg, bi);
+      refill2(q);
     }
     epilogue(gg);
   }
