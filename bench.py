@@ -17,10 +17,13 @@ to evict the 256 MiB last-level cache (reading, not writing, so that the
 evicted lines are clean and the step's reads do not pay for write-backs), so
 the step reads its inputs from HBM; both happen outside the step's HIP-event
 window. Each timed step (rkv_evict_step) is bracketed by two HIP events
-recorded on the launch stream; value = 1000 / mean step milliseconds. A
-second pass of K steps (rkv_evict_step_timed) records an event between
-consecutive kernels and gives each kernel's mean duration, from which the
-roofline fractions are computed; every such mark costs the stream a few
+recorded on the launch stream; value = 1000 / mean step milliseconds. With
+bf16 keys in the order-preserving layout the step is one fused launch (each
+slice's work-group scores, selects and compacts it) plus a small start-slot
+kernel, and that fused kernel is the roofline's dominant kernel. A second
+pass of K steps (rkv_evict_step_timed, which runs the stages as separate
+kernels) records an event between consecutive kernels and gives each
+stage's mean duration and fractions; every such mark costs the stream a few
 microseconds, so that pass is not the one the step rate comes from.
 
 After the timed passes: a warm pass (no flush), the compaction alone with
@@ -52,10 +55,13 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "redundancy_aware_compression_amd", "csrc")
 # sources (and build flags) that determine each kernel's machine code
 KERNEL_SOURCES = {
-    "gram": ["rkv_gram.hip", "rkv_tiles.hpp", "rkv_device.hpp", "rkv_internal.hpp"],
-    "select": ["rkv_select.hip", "rkv_device.hpp", "rkv_internal.hpp"],
-    "compact": ["rkv_compact.hip", "rkv_device.hpp", "rkv_internal.hpp"],
+    "gram": ["rkv_gram.hip", "rkv_select.hpp", "rkv_compact.hpp", "rkv_tiles.hpp", "rkv_device.hpp",
+             "rkv_internal.hpp"],
+    "select": ["rkv_select.hip", "rkv_select.hpp", "rkv_device.hpp", "rkv_internal.hpp"],
+    "compact": ["rkv_compact.hip", "rkv_compact.hpp", "rkv_device.hpp", "rkv_internal.hpp"],
 }
+# the fused step kernel is the scoring kernel's FUSE instance: the same sources
+KERNEL_SOURCES["fused_step"] = KERNEL_SOURCES["gram"]
 
 
 def kernel_source_digest(kernel: str) -> str:
@@ -99,11 +105,12 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
-def measured_mfma_busy(workload: str):
-    """The scoring kernel's MFMA busy fraction on `workload` from the committed
-    rocprofv3 summary (SQ_VALU_MFMA_BUSY_CYCLES over GUI-active cycles of all
-    SIMDs), or None as for measured_traffic."""
-    fields = _profile_fields("gram", os.path.join(PROFILES, f"gram_{workload}_mfma_counters.md"))
+def measured_mfma_busy(workload: str, kernel: str = "gram"):
+    """The MFMA busy fraction of `kernel` (the scoring kernel or the fused
+    step kernel) on `workload` from the committed rocprofv3 summary
+    (SQ_VALU_MFMA_BUSY_CYCLES over GUI-active cycles of all SIMDs), or None as
+    for measured_traffic."""
+    fields = _profile_fields(kernel, os.path.join(PROFILES, f"{kernel}_{workload}_mfma_counters.md"))
     try:
         return float(fields["mfma_busy_fraction"]) if fields else None
     except (KeyError, ValueError):
@@ -212,14 +219,18 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def kernel_table(w, ev_lens, moved, means, holefill=False, peaks=None):
+def kernel_table(w, ev_lens, moved, means, holefill=False, peaks=None, fused_ms=None):
     """Per-kernel algorithmic work per launch, achieved rates against the
     MI355X peaks, and the roofline entry of the dominant kernel. ev_lens: the
     valid lengths of the evicting sequences; moved: rows with keep[j] != j;
-    means: mean milliseconds of the scoring, selection and compaction stages;
-    peaks: measure_peaks()'s result, for the fractions of the measured peaks
-    beside those of the published ones (the MFMA peak is the bf16 one, so it
-    is not applied to fp32 keys)."""
+    means: mean milliseconds of the scoring, selection and compaction stages
+    (the staged pass); peaks: measure_peaks()'s result, for the fractions of
+    the measured peaks beside those of the published ones (the MFMA peak is
+    the bf16 one, so it is not applied to fp32 keys); fused_ms: the mean step
+    time when the step ran as the fused kernel (bf16 keys, order-preserving
+    layout), which is then the dominant kernel: its rate is the scoring
+    flops over the whole launch, and serial_ideal_us is the time of its
+    flops at the MFMA peak plus its bytes at the HBM peak."""
     e = w.elem_bytes
     D, G, A = w.head_dim, w.group, w.obs_window
     per_seq_slices = w.num_layers * w.num_kv_heads
@@ -255,7 +266,25 @@ def kernel_table(w, ev_lens, moved, means, holefill=False, peaks=None):
             k["traffic"] = measured_traffic(name, w.name)
     if not holefill:  # the same fraction from counters: MFMA busy cycles over all SIMDs' cycles
         kernels["gram"]["frac_counters"] = measured_mfma_busy(w.name)
-    dom = max(["gram", "compact"], key=lambda k: kernels[k]["us"])
+    if fused_ms is not None:
+        fb = k3_bytes + k4_bytes + k5_bytes
+        fk = {"us": fused_ms * 1e3, "bound": "mfma", "flops": k3_flops, "bytes": fb,
+              "achieved": k3_flops / (fused_ms * 1e-3) / 1e12, "peak": mfma_peak, "unit": "TFLOP/s",
+              "serial_ideal_us": (k3_flops / (mfma_peak * 1e12) + fb / (HBM_PEAK_GBS * 1e9)) * 1e6,
+              "kernel": "gram_kernel (fused: scoring, selection and compaction of each slice) + start_kernel"}
+        fk["frac"] = fk["achieved"] / fk["peak"]
+        fk["frac_serial_ideal"] = fk["serial_ideal_us"] / fk["us"]
+        if peaks is not None and w.dtype == "bf16":
+            fk["measured_peak"] = peaks["peaks"]["mfma_bf16_tflops"]
+            fk["frac_measured_peak"] = fk["achieved"] / fk["measured_peak"]
+            mr = peaks["peaks"].get("mfma_bf16_random_tflops")
+            if mr:
+                fk["measured_peak_random_operands"] = mr
+                fk["frac_measured_peak_random_operands"] = fk["achieved"] / mr
+        fk["traffic"] = measured_traffic("fused_step", w.name)
+        fk["frac_counters"] = measured_mfma_busy(w.name, "fused_step")
+        kernels["fused_step"] = fk
+    dom = "fused_step" if fused_ms is not None else max(["gram", "compact"], key=lambda k: kernels[k]["us"])
     if holefill:
         kernels["compact"]["kernel"] = "holefill_kernel"
         kernels["compact"]["bound"] = "latency"
@@ -271,6 +300,9 @@ def kernel_table(w, ev_lens, moved, means, holefill=False, peaks=None):
     if dk.get("frac_measured_peak_random_operands") is not None:
         roofline["measured_peak_random_operands"] = dk["measured_peak_random_operands"]
         roofline["frac_measured_peak_random_operands"] = dk["frac_measured_peak_random_operands"]
+    if dk.get("frac_serial_ideal") is not None:
+        roofline["serial_ideal_us"] = dk["serial_ideal_us"]
+        roofline["frac_serial_ideal"] = dk["frac_serial_ideal"]
     return kernels, roofline
 
 
@@ -1058,8 +1090,12 @@ def main():
     mean_ms = sum(step_ms) / len(step_ms)
     peaks = None if args.no_peaks else measure_peaks()
 
+    # bf16 keys in the order-preserving layout: rkv_evict_step is one fused
+    # launch (plus the start-slot kernel); the staged pass gives the stages
+    fused = w.dtype == "bf16" and not holefill
     kernels, roofline = kernel_table(w, [int(cs.lengths[b]) for b in range(w.batch) if cs.lengths[b] > w.budget],
-                                     moved, [sum(x) / len(x) for x in stage_ms], holefill=holefill, peaks=peaks)
+                                     moved, [sum(x) / len(x) for x in stage_ms], holefill=holefill, peaks=peaks,
+                                     fused_ms=mean_ms if fused else None)
     if compact_ms:
         c_ms = sum(compact_ms) / len(compact_ms)
         kb = kernels["compact"]["bytes"]

@@ -253,6 +253,15 @@ rkv_status evict_impl(const rkv_params* p, void* const* k_layers, void* const* v
     if (!stage_events || !stage_events[i]) return 0;
     return (int)hipEventRecord((hipEvent_t)stage_events[i], (hipStream_t)stream);
   };
+  // bf16 keys in the order-preserving layout: one launch scores, selects and
+  // compacts each slice (the timed variant keeps the stages apart, so that
+  // each can be timed)
+  if (p->dtype == RKV_BF16 && !holefill && !sent && !stage_events) {
+    RKV_TRY(rkv::launch_fused_step(g, p->dtype, kl, vl, obs_q, seq_start, w.importance, w.rowmean, w.counts, w.keep,
+                                   stream, imp_acc));
+    *n_slots = p->budget;
+    return RKV_OK;
+  }
   RKV_TRY(mark(0));
   if (sent)
     RKV_TRY(rkv::launch_sentence_penalty(sent->vectors, sent->n_sent, p->batch, sent->s_max, sent->dim, sent->tau_s,

@@ -52,6 +52,8 @@
 // loads the next group's rows.
 #include <type_traits>
 
+#include "rkv_compact.hpp"
+#include "rkv_select.hpp"
 #include "rkv_tiles.hpp"
 
 namespace rkv {
@@ -156,6 +158,39 @@ __device__ inline float sum8_dpp(float v) {
   return v;
 }
 
+// The rest of the eviction step for one slice, by the work-group that scored
+// it (FUSE): the selection from the counts, row means and importance the
+// scoring pass just wrote, then the in-place compaction of the slice's K and
+// V rows, while its keys are still in the caches. The keys and the
+// selection's histograms take the LDS of the row ring (`lds`). seq_start is
+// left alone: other work-groups of the launch still read it (start_kernel
+// writes it afterwards).
+template <typename T>
+__device__ inline void fused_tail(const Geom& g, int slice, int l, int b, int h, int s0, int N, const LayerPtrs& k,
+                                  const LayerPtrs& v, const float* importance, const int32_t* counts,
+                                  const float* rowmean, int32_t* keep, char* lds) {
+  constexpr int RB = kHeadDim * Elem<T>::kBytes;
+  constexpr size_t KEYS = (size_t)RKV_MAX_CAPACITY * 4;
+  // every store of this work-group's scoring is complete before any wave reads
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  select_slice<true, false>(g, slice, b, s0, N, importance, nullptr, counts, rowmean, keep, nullptr, nullptr, nullptr,
+                            nullptr, 0, (uint32_t*)lds, *(SelectLds*)(lds + KEYS));
+  __builtin_amdgcn_s_waitcnt(0);  // the keep row is written before it is read
+  __syncthreads();
+  const int32_t* krow = keep + (size_t)slice * g.budget;
+  const size_t off = ((size_t)b * g.H + h) * g.capacity * (size_t)RB;
+  compact_rows<T>((char*)k.p[l] + off, krow, g);
+  compact_rows<T>((char*)v.p[l] + off, krow, g);
+}
+
+// A sequence's first valid slot after the fused step, from the keep row of
+// its (layer 0, KV head 0) slice.
+__global__ void start_kernel(Geom g, const int32_t* __restrict__ keep, int32_t* __restrict__ seq_start) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < g.batch) seq_start[b] = leading_unkept(keep + (size_t)b * g.H * g.budget, g.budget);
+}
+
 // GATHER: the slice's valid tokens are virtual slots [s0, n_slots); virtual
 // slot v < budget is stored at physical slot order[v], v >= budget at v (the
 // layout the hole-filling compaction keeps). The row loads gather physical
@@ -164,14 +199,19 @@ __device__ inline float sum8_dpp(float v) {
 // captured, imp_acc [slices][G][capacity] (sums over the observation window):
 // I = max over the group of the sum / alpha. The queries are not read and the
 // logit work is left out; only with GATHER = false.
-template <typename T, bool GATHER, bool CAPT>
-__global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k, const void* __restrict__ obs_q,
+// FUSE: the work-group goes on to the slice's selection and compaction
+// (fused_tail; only with GATHER = false; v and keep are used only then).
+template <typename T, bool GATHER, bool CAPT, bool FUSE>
+__global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k, LayerPtrs v,
+                                                            const void* __restrict__ obs_q,
                                                             const int32_t* __restrict__ seq_start,
                                                             const int32_t* __restrict__ order,
                                                             const float* __restrict__ imp_acc,
                                                             float* __restrict__ importance,
-                                                            float* __restrict__ rowmean, int32_t* __restrict__ counts) {
+                                                            float* __restrict__ rowmean, int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ keep) {
   static_assert(!(GATHER && CAPT), "captured importance is indexed by virtual slot only without GATHER");
+  static_assert(!(GATHER && FUSE), "the fused step keeps the order-preserving layout");
   using S = Stage<T>;
   using TL = Tile16<T>;
   constexpr int RB = S::RB;
@@ -186,12 +226,17 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   constexpr int KA = 4;  // GATHER: refills between an ORD load and its use
   __shared__ __align__(16) int ord_lds[GATHER ? KA : 1][kGramWaves][8];  // GATHER: order entries of a wave's rows
   static_assert(kGramWaves * (2 * 16 * 2 + kHeadDim) * 4 <= 32 * RB, "merge scratch fits the s tile");
+  static_assert((size_t)RKV_MAX_CAPACITY * 4 + sizeof(SelectLds) <= sizeof(rows_lds), "the fused tail's LDS");
+  static_assert(kGramThreads == kSelectThreads && kGramThreads == kCompactThreads, "one work-group size");
 
   const int slice = xcd_remap(blockIdx.x, gridDim.x);
   int l, b, h, s0, N;
   slice_coords(g, slice, l, b, h);
   seq_range(g, seq_start, b, s0, N);
-  if (N <= g.budget) return;
+  if (N <= g.budget) {
+    if constexpr (FUSE) fused_tail<T>(g, slice, l, b, h, s0, N, k, v, importance, counts, rowmean, keep, rows_lds);
+    return;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, col = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases go to scalar registers
@@ -834,6 +879,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
     }
     epilogue(gg);
   }
+  if constexpr (FUSE) fused_tail<T>(g, slice, l, b, h, s0, N, k, v, importance, counts, rowmean, keep, rows_lds);
 }
 
 // rbar = 0 for protected tokens (fewer than beta newer similar tokens), else
@@ -859,8 +905,8 @@ int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q,
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid(slices), block(kGramThreads);
 #define RKV_GRAM(T, GA, CA)                                                                                   \
-  RKV_LAUNCH((gram_kernel<T, GA, CA>), grid, block, 0, s, g, k, obs_q, seq_start, order, imp_acc, \
-                     importance, rowmean, counts)
+  RKV_LAUNCH((gram_kernel<T, GA, CA, false>), grid, block, 0, s, g, k, k, obs_q, seq_start, order, imp_acc, \
+                     importance, rowmean, counts, (int32_t*)nullptr)
   if (dtype != RKV_BF16) return (int)hipErrorInvalidValue;  // fp32 keys: launch_score_f32
   if (order)
     RKV_GRAM(bf16_t, true, false);
@@ -869,6 +915,26 @@ int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q,
   else
     RKV_GRAM(bf16_t, false, false);
 #undef RKV_GRAM
+  return 0;
+}
+
+int launch_fused_step(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const void* obs_q,
+                      int32_t* seq_start, float* importance, float* rowmean, int32_t* counts, int32_t* keep,
+                      void* stream, const float* imp_acc) {
+  const int slices = g.L * g.batch * g.H;
+  if (slices == 0) return 0;
+  if (dtype != RKV_BF16 || g.capacity > RKV_MAX_CAPACITY) return (int)hipErrorInvalidValue;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid(slices), block(kGramThreads);
+  if (imp_acc)
+    RKV_LAUNCH((gram_kernel<bf16_t, false, true, true>), grid, block, 0, s, g, k, v, obs_q,
+                       (const int32_t*)seq_start, (const int32_t*)nullptr, imp_acc, importance, rowmean, counts,
+                       keep);
+  else
+    RKV_LAUNCH((gram_kernel<bf16_t, false, false, true>), grid, block, 0, s, g, k, v, obs_q,
+                       (const int32_t*)seq_start, (const int32_t*)nullptr, imp_acc, importance, rowmean, counts,
+                       keep);
+  RKV_LAUNCH(start_kernel, dim3((g.batch + 255) / 256), dim3(256), 0, s, g, (const int32_t*)keep, seq_start);
   return 0;
 }
 

@@ -136,6 +136,14 @@ int launch_compact_holefill(const Geom& g, int dtype, const LayerPtrs& k, const 
                             int32_t* order, int32_t* seq_start, void* stream);
 int launch_compact(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const int32_t* keep,
                    int32_t* seq_start, void* stream);
+// The whole order-preserving step for bf16 keys in one scoring launch
+// (rkv_gram.hip): each slice's work-group scores it, selects (keep) and
+// compacts its K and V rows; a second launch then writes seq_start. Same
+// results as launch_gram + launch_select (counts and row means) +
+// launch_compact. Needs capacity <= RKV_MAX_CAPACITY.
+int launch_fused_step(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const void* obs_q,
+                      int32_t* seq_start, float* importance, float* rowmean, int32_t* counts, int32_t* keep,
+                      void* stream, const float* imp_acc);
 
 // RKV_DEBUG device checks (rkv_debug.hip): clears flags[0], then ORs into
 // it kDbgSeqStart when some seq_start[b] lies outside [0, n_slots],

@@ -48,6 +48,10 @@ int launch_compact_holefill(const Geom&, int, const LayerPtrs&, const LayerPtrs&
 int launch_compact(const Geom&, int, const LayerPtrs&, const LayerPtrs&, const int32_t*, int32_t*, void*) {
   launched("launch_compact");
 }
+int launch_fused_step(const Geom&, int, const LayerPtrs&, const LayerPtrs&, const void*, int32_t*, float*, float*,
+                      int32_t*, int32_t*, void*, const float*) {
+  launched("launch_fused_step");
+}
 int launch_debug_check(const Geom&, int, const LayerPtrs&, const LayerPtrs&, const void*, const int32_t*,
                        const int32_t*, uint32_t*, void*) {
   launched("launch_debug_check");

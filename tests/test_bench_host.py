@@ -65,3 +65,23 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr or "single" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_fused_step_is_the_dominant_kernel():
+    """With the fused step the roofline describes that one launch: the scoring
+    flops over its whole duration, and the time its flops at the MFMA peak
+    plus its bytes (scoring, selection and compaction) at the HBM peak would
+    take."""
+    w = synth.WORKLOADS["qwen14b_b8"]
+    kernels, roofline = bench.kernel_table(w, [4224] * 8, 1000, [7.7, 0.09, 2.28], fused_ms=9.0)
+    f = kernels["fused_step"]
+    assert roofline["kernel"] == "fused_step" and roofline["bound"] == "mfma" and roofline["unit"] == "TFLOP/s"
+    assert abs(f["achieved"] - kernels["gram"]["flops"] / 9.0e-3 / 1e12) < 1e-6
+    assert f["bytes"] == kernels["gram"]["bytes"] + kernels["select"]["bytes"] + kernels["compact"]["bytes"]
+    ideal_us = (kernels["gram"]["flops"] / 2.5e15 + f["bytes"] / 8e12) * 1e6
+    assert abs(f["serial_ideal_us"] - ideal_us) < 1e-6
+    assert abs(roofline["frac_serial_ideal"] - ideal_us / 9000.0) < 1e-12
+    assert abs(roofline["frac"] - f["achieved"] / 2500.0) < 1e-12
+    # without it, the staged scoring kernel stays the dominant one
+    _, staged = bench.kernel_table(w, [4224] * 8, 1000, [7.7, 0.09, 2.28])
+    assert staged["kernel"] == "gram"

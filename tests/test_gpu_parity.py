@@ -260,6 +260,40 @@ def test_evict_step(name):
     print(f"{name}: {len(refs)} slices checked; kept-set differences inside the band: {ndiff}")
 
 
+@pytest.mark.parametrize("name", ["small_ragged", "small_g5", "small_a4", "small_negtau", "max_capacity",
+                                  "llama8b_b1"])
+def test_fused_step_equals_staged(name):
+    """rkv_evict_step scores, selects and compacts each slice in one launch
+    (bf16 keys); rkv_evict_step_timed runs the same work as three kernels.
+    Both leave bit-identical K and V caches, start slots and keep rows, for
+    evicting and non-evicting sequences alike."""
+    import redundancy_aware_compression_amd as rkv
+
+    torch, dev = _gpu.torch_dev()
+    cs, _ = cache_of(name)
+    w = cs.w
+    p = _gpu.params_of(w)
+    wsb = rkv.rkv_workspace_bytes(p)
+    koff = rkv.rkv_workspace_keep_offset(p)
+    out = []
+    for staged in (False, True):
+        dc = _gpu.DevCache.of(cs)
+        ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+        if staged:
+            st, ns = rkv.rkv_evict_step_timed(p, dc.k_layers(), dc.v_layers(), dc.Q, dc.seq_start, cs.n_slots, ws,
+                                              wsb, [0, 0, 0, 0])
+        else:
+            st, ns = rkv.rkv_evict_step(p, dc.k_layers(), dc.v_layers(), dc.Q, dc.seq_start, cs.n_slots, ws, wsb)
+        torch.cuda.synchronize()
+        assert ns == w.budget
+        keep = ws[koff:koff + w.slices * w.budget * 4].view(torch.int32).cpu().numpy()
+        out.append((_gpu.to_host(dc.K, cs.K.dtype).view(np.uint8), _gpu.to_host(dc.V, cs.V.dtype).view(np.uint8),
+                    dc.seq_start.cpu().numpy(), keep))
+        del dc
+    for what, a, b in zip(("K", "V", "seq_start", "keep"), *out):
+        assert np.array_equal(a, b), f"{name}: fused and staged steps differ in {what}"
+
+
 def test_evict_step_degenerate():
     """One evicting batch with an empty sequence (N = 0), a one-token sequence
     and zero keys in an evicting sequence, one of them in the observation
