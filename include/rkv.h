@@ -194,7 +194,10 @@ rkv_status rkv_compact(const rkv_params* p, void* const* k_layers, void* const* 
  * If *n_slots < budget + buffer nothing is launched or written (RKV_OK).
  * Otherwise scoring, selection and compaction run on `stream` and *n_slots
  * becomes budget; afterwards sequence b holds min(N_b, budget) tokens in
- * slots [seq_start[b], budget), in their original order.
+ * slots [seq_start[b], budget), in their original order. With bf16 keys the
+ * three stages run as one launch (each slice's work-group scores, selects
+ * and compacts it) followed by a small kernel that writes seq_start; the
+ * results are bit-identical to the staged kernels of rkv_evict_step_timed.
  *   k_layers, v_layers  HOST arrays of device pointers (modified in place)
  *   obs_q      observation queries (read only)
  *   seq_start  in/out
@@ -210,8 +213,9 @@ rkv_status rkv_evict_step(const rkv_params* p, void* const* k_layers, void* cons
  * entries are skipped). Event s is recorded on `stream` right before stage s
  * is enqueued — 0 scoring (key statistics, Gram, importance and row mean in
  * one kernel), 1 selection, 2 compaction — and event 3 after the last one.
- * On the no-op path no event is recorded. Everything else is exactly
- * rkv_evict_step.
+ * The stages always run as separate kernels here (rkv_evict_step fuses them
+ * for bf16 keys), with the same results. On the no-op path no event is
+ * recorded. Everything else is exactly rkv_evict_step.
  */
 rkv_status rkv_evict_step_timed(const rkv_params* p, void* const* k_layers, void* const* v_layers,
                                 const void* obs_q, int32_t* seq_start, int32_t* n_slots, void* ws, size_t ws_bytes,
