@@ -399,7 +399,8 @@ def sweep_main(args, w):
     st_rounds = [x for x in staged if x[0] >= SWEEP_STEADY_FROM] or staged
     means = [percentile([x[1][i] for x in st_rounds], 50) for i in range(3)]
     mv_med = int(percentile([x[2] for x in st_rounds], 50))
-    kernels, roofline = kernel_table(w, [w.budget + w.buffer] * w.batch, mv_med, means, holefill=holefill)
+    kernels, roofline = kernel_table(w, [w.budget + w.buffer] * w.batch, mv_med, means, holefill=holefill,
+                                     fused_ms=med if w.dtype == "bf16" and not holefill else None)
     out = {
         "metric": METRIC,
         "value": 1000.0 / med,
