@@ -482,9 +482,9 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   // Gram work, so one barrier covers BPB blocks (their norms written by other
   // waves, the next BPB blocks landed, the stages of the previous BPB free).
   // The ring holds BPB blocks in Gram work, BPB in the pre-pass and at least
-  // BPB in flight. The gathered stream keeps one block per barrier (its
-  // order-table loads are counted per refill).
-  constexpr int BPB = GATHER ? 1 : 2;
+  // BPB in flight. (The gathered stream's order-table loads are counted per
+  // refill, in the refills' order, which the pairs do not change.)
+  constexpr int BPB = 2;
   static_assert(S::COUNT >= 3 * BPB, "ring depth for the blocks per barrier");
   auto pre_any = [&](int x) {
     if (x < nrb)
@@ -495,7 +495,7 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
 
   // blocks 0 .. BPB - 1 and the queries (issued after ROW(0), before ROW(1))
   if constexpr (GATHER)
-    wait_vm(pro_n == 1 ? 0 : end_row(pro_n - 1) - 2 * S::PER - o0);
+    wait_vm(pro_n == 1 ? 0 : end_row(pro_n - 1) - max(end_row(min(BPB, pro_n) - 1), o0 + 2 * S::PER));
   else
     wait_later_blocks<S::PER>(pro_n - min(BPB, pro_n));
   __syncthreads();
