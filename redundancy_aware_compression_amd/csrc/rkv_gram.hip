@@ -50,6 +50,11 @@
 // taken in registers) and the row mean of S through
 // sum_{j != i} S_ij = khat_i . s - khat_i . khat_i, while the ring already
 // loads the next group's rows.
+//
+// The fused eviction step (FUSE) keeps the work-group on its slice after the
+// last group: it selects the slice's tokens and compacts its K and V rows in
+// place (fused_tail), so that each compute unit's copy phases fall between
+// its scoring phases instead of all copies running after all scoring.
 #include <type_traits>
 
 #include "rkv_compact.hpp"
