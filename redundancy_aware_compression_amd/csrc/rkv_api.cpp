@@ -256,9 +256,13 @@ rkv_status evict_impl(const rkv_params* p, void* const* k_layers, void* const* v
   // bf16 keys in the order-preserving layout: one launch scores, selects and
   // compacts each slice (the timed variant keeps the stages apart, so that
   // each can be timed)
-  if (p->dtype == RKV_BF16 && !holefill && !sent && !stage_events) {
+  if (p->dtype == RKV_BF16 && !holefill && !stage_events) {
+    if (sent)
+      RKV_TRY(rkv::launch_sentence_penalty(sent->vectors, sent->n_sent, p->batch, sent->s_max, sent->dim,
+                                           sent->tau_s, sent->penalty, stream));
     RKV_TRY(rkv::launch_fused_step(g, p->dtype, kl, vl, obs_q, seq_start, w.importance, w.rowmean, w.counts, w.keep,
-                                   stream, imp_acc));
+                                   stream, imp_acc, sent ? sent->penalty : nullptr, sent ? sent->sent_id : nullptr,
+                                   sent ? sent->s_max : 0));
     *n_slots = p->budget;
     return RKV_OK;
   }

@@ -169,24 +169,41 @@ __device__ inline float sum8_dpp(float v) {
 // V rows, while its keys are still in the caches. The keys and the
 // selection's histograms take the LDS of the row ring (`lds`). seq_start is
 // left alone: other work-groups of the launch still read it (start_kernel
-// writes it afterwards).
+// writes it afterwards). With sent_id (SkipKV's sentence deduction, SkipKV
+// notes page, summary table row "final eviction score") Z loses the
+// sentence penalties and the sentence-id sidecar moves with the rows.
 template <typename T>
 __device__ inline void fused_tail(const Geom& g, int slice, int l, int b, int h, int s0, int N, const LayerPtrs& k,
                                   const LayerPtrs& v, const float* importance, const int32_t* counts,
-                                  const float* rowmean, int32_t* keep, char* lds) {
+                                  const float* rowmean, int32_t* keep, const float* sent_pen, int32_t* sent_id,
+                                  int s_max, char* lds) {
   constexpr int RB = kHeadDim * Elem<T>::kBytes;
   constexpr size_t KEYS = (size_t)RKV_MAX_CAPACITY * 4;
   // every store of this work-group's scoring is complete before any wave reads
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  select_slice<true, false>(g, slice, b, s0, N, importance, nullptr, counts, rowmean, keep, nullptr, nullptr, nullptr,
-                            nullptr, 0, (uint32_t*)lds, *(SelectLds*)(lds + KEYS));
+  if (sent_id)  // (uniform)
+    select_slice<true, true>(g, slice, b, s0, N, importance, nullptr, counts, rowmean, keep, nullptr, nullptr,
+                             sent_pen, sent_id, s_max, (uint32_t*)lds, *(SelectLds*)(lds + KEYS));
+  else
+    select_slice<true, false>(g, slice, b, s0, N, importance, nullptr, counts, rowmean, keep, nullptr, nullptr,
+                              nullptr, nullptr, 0, (uint32_t*)lds, *(SelectLds*)(lds + KEYS));
   __builtin_amdgcn_s_waitcnt(0);  // the keep row is written before it is read
   __syncthreads();
   const int32_t* krow = keep + (size_t)slice * g.budget;
   const size_t off = ((size_t)b * g.H + h) * g.capacity * (size_t)RB;
   compact_rows<T>((char*)k.p[l] + off, krow, g);
   compact_rows<T>((char*)v.p[l] + off, krow, g);
+  if (sent_id) {  // ids[j] <- ids[keep[j]], -1 where keep[j] < 0: every read staged in LDS before any write
+    int32_t* irow = sent_id + (size_t)slice * g.capacity;
+    int32_t* stage = (int32_t*)lds;  // the selection's keys are no longer needed
+    for (int j = threadIdx.x; j < g.budget; j += blockDim.x) {
+      const int kj = krow[j];
+      stage[j] = (kj >= 0 && kj < g.n_slots) ? irow[kj] : -1;
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < g.budget; j += blockDim.x) irow[j] = stage[j];
+  }
 }
 
 // A sequence's first valid slot after the fused step, from the keep row of
@@ -214,7 +231,9 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
                                                             const float* __restrict__ imp_acc,
                                                             float* __restrict__ importance,
                                                             float* __restrict__ rowmean, int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ keep) {
+                                                            int32_t* __restrict__ keep,
+                                                            const float* __restrict__ sent_pen,
+                                                            int32_t* __restrict__ sent_id, int s_max) {
   static_assert(!(GATHER && CAPT), "captured importance is indexed by virtual slot only without GATHER");
   static_assert(!(GATHER && FUSE), "the fused step keeps the order-preserving layout");
   using S = Stage<T>;
@@ -239,7 +258,8 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
   slice_coords(g, slice, l, b, h);
   seq_range(g, seq_start, b, s0, N);
   if (N <= g.budget) {
-    if constexpr (FUSE) fused_tail<T>(g, slice, l, b, h, s0, N, k, v, importance, counts, rowmean, keep, rows_lds);
+    if constexpr (FUSE) fused_tail<T>(g, slice, l, b, h, s0, N, k, v, importance, counts, rowmean, keep, sent_pen, sent_id,
+                                            s_max, rows_lds);
     return;
   }
 
@@ -884,7 +904,8 @@ __global__ __launch_bounds__(kGramThreads) void gram_kernel(Geom g, LayerPtrs k,
     }
     epilogue(gg);
   }
-  if constexpr (FUSE) fused_tail<T>(g, slice, l, b, h, s0, N, k, v, importance, counts, rowmean, keep, rows_lds);
+  if constexpr (FUSE) fused_tail<T>(g, slice, l, b, h, s0, N, k, v, importance, counts, rowmean, keep, sent_pen, sent_id,
+                                            s_max, rows_lds);
 }
 
 // rbar = 0 for protected tokens (fewer than beta newer similar tokens), else
@@ -911,7 +932,7 @@ int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q,
   const dim3 grid(slices), block(kGramThreads);
 #define RKV_GRAM(T, GA, CA)                                                                                   \
   RKV_LAUNCH((gram_kernel<T, GA, CA, false>), grid, block, 0, s, g, k, k, obs_q, seq_start, order, imp_acc, \
-                     importance, rowmean, counts, (int32_t*)nullptr)
+                     importance, rowmean, counts, (int32_t*)nullptr, (const float*)nullptr, (int32_t*)nullptr, 0)
   if (dtype != RKV_BF16) return (int)hipErrorInvalidValue;  // fp32 keys: launch_score_f32
   if (order)
     RKV_GRAM(bf16_t, true, false);
@@ -925,7 +946,7 @@ int launch_gram(const Geom& g, int dtype, const LayerPtrs& k, const void* obs_q,
 
 int launch_fused_step(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const void* obs_q,
                       int32_t* seq_start, float* importance, float* rowmean, int32_t* counts, int32_t* keep,
-                      void* stream, const float* imp_acc) {
+                      void* stream, const float* imp_acc, const float* sent_pen, int32_t* sent_id, int s_max) {
   const int slices = g.L * g.batch * g.H;
   if (slices == 0) return 0;
   if (dtype != RKV_BF16 || g.capacity > RKV_MAX_CAPACITY) return (int)hipErrorInvalidValue;
@@ -934,11 +955,11 @@ int launch_fused_step(const Geom& g, int dtype, const LayerPtrs& k, const LayerP
   if (imp_acc)
     RKV_LAUNCH((gram_kernel<bf16_t, false, true, true>), grid, block, 0, s, g, k, v, obs_q,
                        (const int32_t*)seq_start, (const int32_t*)nullptr, imp_acc, importance, rowmean, counts,
-                       keep);
+                       keep, sent_pen, sent_id, s_max);
   else
     RKV_LAUNCH((gram_kernel<bf16_t, false, false, true>), grid, block, 0, s, g, k, v, obs_q,
                        (const int32_t*)seq_start, (const int32_t*)nullptr, imp_acc, importance, rowmean, counts,
-                       keep);
+                       keep, sent_pen, sent_id, s_max);
   RKV_LAUNCH(start_kernel, dim3((g.batch + 255) / 256), dim3(256), 0, s, g, (const int32_t*)keep, seq_start);
   return 0;
 }

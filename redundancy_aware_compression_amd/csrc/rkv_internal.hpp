@@ -140,10 +140,12 @@ int launch_compact(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs
 // (rkv_gram.hip): each slice's work-group scores it, selects (keep) and
 // compacts its K and V rows; a second launch then writes seq_start. Same
 // results as launch_gram + launch_select (counts and row means) +
-// launch_compact. Needs capacity <= RKV_MAX_CAPACITY.
+// launch_compact (+ launch_compact_ids with sent_id: the sentence penalties,
+// computed before, enter the selection). Needs capacity <= RKV_MAX_CAPACITY.
 int launch_fused_step(const Geom& g, int dtype, const LayerPtrs& k, const LayerPtrs& v, const void* obs_q,
                       int32_t* seq_start, float* importance, float* rowmean, int32_t* counts, int32_t* keep,
-                      void* stream, const float* imp_acc);
+                      void* stream, const float* imp_acc, const float* sent_pen = nullptr, int32_t* sent_id = nullptr,
+                      int s_max = 0);
 
 // RKV_DEBUG device checks (rkv_debug.hip): clears flags[0], then ORs into
 // it kDbgSeqStart when some seq_start[b] lies outside [0, n_slots],

@@ -49,7 +49,7 @@ int launch_compact(const Geom&, int, const LayerPtrs&, const LayerPtrs&, const i
   launched("launch_compact");
 }
 int launch_fused_step(const Geom&, int, const LayerPtrs&, const LayerPtrs&, const void*, int32_t*, float*, float*,
-                      int32_t*, int32_t*, void*, const float*) {
+                      int32_t*, int32_t*, void*, const float*, const float*, int32_t*, int) {
   launched("launch_fused_step");
 }
 int launch_debug_check(const Geom&, int, const LayerPtrs&, const LayerPtrs&, const void*, const int32_t*,
