@@ -44,6 +44,9 @@ SMALL = {
     # scoring kernel's 64-row blocks: rows past a slice must never count as similar, whatever tau's sign
     "small_negtau": synth.small("small_negtau", 124, num_layers=1, batch=3, num_kv_heads=2, group=4, budget=256,
                                 buffer=100, lengths=("uniform", 200, 356), tau=-0.25),
+    # fp32 keys over three compaction chunks of 256 rows (an odd count, a partial last chunk), ragged
+    "f32_chunks": synth.small("f32_chunks", 126, num_layers=1, batch=2, num_kv_heads=2, group=2, budget=700,
+                              dtype="f32", lengths=("uniform", 500, 828)),
 }
 
 # the full-size workloads; their slices are sampled by sample_of
@@ -180,9 +183,11 @@ def _random_keep(rng, B, n_slots, N):
     return row
 
 
-@pytest.mark.parametrize("name", ["small_ragged", "small_a4", "single_f32", "llama8b_b1"])
+@pytest.mark.parametrize("name", ["small_ragged", "small_a4", "single_f32", "f32_chunks", "small_long", "llama8b_b1"])
 def test_compact_bit_exact(name):
-    """In-place compaction vs a plain gather of the pre-step bytes, adversarial keep patterns."""
+    """In-place compaction vs a plain gather of the pre-step bytes, adversarial keep patterns.
+    The compaction moves rows in chunks (512 rows of bf16, 256 of fp32) with the next chunk's loads in
+    flight during a chunk's stores: small_long spans 11 chunks, f32_chunks 3."""
     import redundancy_aware_compression_amd as rkv
 
     torch, dev = _gpu.torch_dev()
