@@ -3,8 +3,9 @@
 //
 // Safety of the in-place gather: keep is ascending with keep[j] >= j, so when
 // destinations are processed in ascending chunks, a chunk's writes land below
-// every source of every later chunk, and its own sources are all read before
-// any of its writes (loads, a full vmcnt wait, then a barrier, then stores).
+// every source of every later chunk (which may therefore be loaded while the
+// chunk stores), and its own sources are all read before any of its writes
+// (its loads returned in every thread, then a barrier, then its stores).
 // Rows with keep[j] == j are skipped. R-KV notes page
 // (yoonschallenge.tistory.com/1236), Q&A part 2, cause 3: the selected KV is
 // copied into the new cache; cause 4: re-allocation and re-arrangement after
